@@ -1,0 +1,189 @@
+/* int8attn.h -- C ABI of the MI355X (gfx950) INT8-KV paged attention library.
+ *
+ * Attention reads a paged cache of int8 K/V codes with one fp32 absmax scale per
+ * (token, KV head) directly; no dequantized K/V tensor ever exists.
+ *
+ * Sources (cited by page title and section):
+ *  [DCU]   "INT8 KV and INT8 MMAC attention on a gfx936 DCU" (gfx936 DCU上实现INT8 KV与
+ *          INT8 MMAC Attention推理优化, sourcefind forum article)
+ *  [DOT4]  "dot4-flash-attention" (GitHub README)
+ *  [QSA]   "#3381 prompt QSA attention without the decode kernel's split and merge"
+ *          (strata engine pull request)
+ *  [R4D]   "ROCm/RDNA4 (gfx1201) vLLM: native HIP kernels, baked-in quantizers and
+ *          tuner" (vLLM docs page, kernel-lessons part)
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions common to every entry point
+ *  - Every pointer argument except `stream` is a DEVICE pointer (hipMalloc'd or
+ *    torch-owned GPU memory). The caller owns every buffer; the library keeps no
+ *    reference after the call returns and allocates nothing.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).
+ *    Work is enqueued asynchronously; no call synchronizes.
+ *  - Return value: I8A_OK (0) on success, a negative I8A_E* code on error. On an
+ *    argument error nothing is enqueued and no output is touched. The message of the
+ *    last error on the calling thread is available from int8attn_last_error().
+ *  - Thread-safe: no global mutable state except the thread-local error message.
+ *  - v1 shape contract: head_dim == 256, page size 16 tokens, n_q_heads ==
+ *    6 * n_kv_heads (GQA groups of 6, query head h reads KV head h / 6) [DOT4 contract
+ *    "D=256, GQA required"; DCU §1.1 geometry 24 q heads over 4 KV heads]. Any other
+ *    shape returns I8A_EUNSUPPORTED.
+ *  - Inputs must be finite. Contexts are >= 1 token.
+ *
+ * ---------------------------------------------------------------------------
+ * Paged cache layout (the contract between the writer and the readers)
+ *  A page holds 16 consecutive tokens of one sequence; slot = page * 16 + offset.
+ *  Each (page p, KV head h) owns one contiguous 4096-byte block of K codes, one of V
+ *  codes, and 16 fp32 scales of each. With H = n_kv_heads, the element (p, h, token
+ *  offset o in 0..15, dim d in 0..255) lives at:
+ *
+ *    k_cache byte  ((p*H + h)*16 + d/16)*256 + o*16 + d%16
+ *        = [page][head][d/16][o][d%16]: 16 dims of one token are one 16-byte run
+ *          [DCU §2.3 chooses the same K blocking, [blocks, 4, 16, block_size, 16]].
+ *    v_cache byte  (p*H + h)*4096 + (d/64)*1024 + (o/4)*256 + (d%16)*16
+ *                  + ((d/16)%4)*4 + o%4
+ *        = [page][head][d/64][o/4][d%16][(d/16)%4][o%4]: V is token-contiguous in runs
+ *          of 4 tokens per dim [DCU §2.3 keeps V token-contiguous for the PV product];
+ *          one 16-byte run holds 4 tokens x 4 dims whose dims are 16 apart, which is
+ *          exactly one lane's operand bytes of the PV matrix product.
+ *    k_scale / v_scale float  (p*H + h)*16 + o      [DCU §2.3: FP32 scales apart from
+ *          the codes]
+ *
+ *  Per token and per layer this is 2*4*256 + 2*4*4 = 2080 bytes at H = 4 [DCU §1.1].
+ *  The library never reads a slot that no table entry covers with a valid position.
+ *
+ * Quantization rule (bit-exact contract) [DCU §2.1]
+ *  For one row x of 256 values (one token of one K, V or Q head), in IEEE fp32:
+ *    amax  = max |x_i|
+ *    scale = amax / 127           (correctly rounded fp32 division)
+ *    code  = clamp(rint(x_i / scale), -127, 127)   (x_i / scale correctly rounded,
+ *                                                    rint = round half to even)
+ *  If scale == 0 (amax == 0, or amax/127 underflows) the codes are all 0 and the
+ *  stored scale is 0.0. Dequantized value = code * scale.
+ */
+#ifndef INT8ATTN_H
+#define INT8ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define I8A_OK            0
+#define I8A_EINVAL       -1  /* null pointer, negative or zero size, bad dtype flag    */
+#define I8A_EUNSUPPORTED -2  /* shape outside the v1 contract (head_dim, GQA group)    */
+#define I8A_EWORKSPACE   -3  /* decode workspace too small                             */
+#define I8A_ELAUNCH      -4  /* the HIP runtime reported an error at launch            */
+
+#define I8A_DTYPE_F32  0
+#define I8A_DTYPE_BF16 1
+
+/* Message of the last error returned on this thread ("" if none). The pointer stays
+ * valid until the next call on the same thread. */
+const char* int8attn_last_error(void);
+
+/* Library version, (major << 16) | minor. */
+int int8attn_version(void);
+
+/* kv_quant_write -- quantize new K and V rows and write them into the paged cache.
+ * [DCU §2.1 rule; §2.2 fused producer: absmax, scale, quantize, paged INT8 write and
+ *  scale write in one kernel; DOT4 "K packing" at cache-write time.]
+ *
+ *  k, v          input rows [n_tokens][n_kv_heads][head_dim], fp32 or bf16 (in_dtype),
+ *                row-major and contiguous. K and V rows are quantized independently.
+ *  slot_mapping  int32 [n_tokens]: destination slot of each token. A slot < 0 or
+ *                >= num_pages*16 skips that token (nothing is written for it). Two
+ *                tokens with the same slot: unspecified which one wins.
+ *  k_cache, v_cache   int8 [num_pages * n_kv_heads * 4096] in the layout above.
+ *  k_scale, v_scale   fp32 [num_pages * n_kv_heads * 16].
+ *  Only the slots named by slot_mapping are written; everything else is untouched.
+ *  n_tokens == 0 is a no-op returning I8A_OK. */
+int kv_quant_write(const void* k, const void* v, int in_dtype,
+                   int n_tokens, int n_kv_heads, int head_dim,
+                   const int32_t* slot_mapping,
+                   int8_t* k_cache, int8_t* v_cache,
+                   float* k_scale, float* v_scale,
+                   int num_pages, void* stream);
+
+/* q_quant -- quantize bf16 query rows with the same rule [DCU §2.2: the query is
+ * quantized once per token and head]. The attention entry points do this internally
+ * with the same device routine; this entry exposes it for inspection.
+ *  q_bf16  [n_rows][head_dim] bf16 bits (row = one (token, q head));
+ *  codes   int8 [n_rows][head_dim];  scales fp32 [n_rows]. */
+int q_quant(const uint16_t* q_bf16, int n_rows, int head_dim,
+            int8_t* codes, float* scales, void* stream);
+
+/* Bytes of scratch attn_decode needs for this batch shape: the per-partition partial
+ * softmax states, num_seqs * n_q_heads * ceil(max_context_len/512) * (2 + head_dim)
+ * floats, rounded up to 256 bytes. Sizing for the largest max_context_len lets smaller
+ * calls reuse one buffer (their partials pack into a prefix). Returns 0 for invalid
+ * arguments. */
+size_t attn_decode_workspace_bytes(int num_seqs, int max_context_len,
+                                   int n_q_heads, int head_dim);
+
+/* attn_decode -- one new query token per sequence against its paged INT8 K/V.
+ * [DOT4 route table: split-K stage 1 over 512-row splits + stage 2 merge; DCU §3.3:
+ *  paged INT8 K/V, per-token scales, INT8 query + query scale, block table, partitions
+ *  then a merge of softmax states and outputs; DCU §1.3 score formula.]
+ *
+ *  Stage 1: for every (sequence, KV head, 512-row partition) the query rows of the
+ *  group are quantized (q_quant rule), scores = int8(Q).int8(K) * sQ * sK * sm_scale
+ *  (exact int32 dot, scales applied after accumulation), an fp32 softmax over the
+ *  partition, and the weighted sum of V in fp32 precision; the partial state
+ *  (max, sum, unnormalised output) goes to `workspace`.
+ *  Stage 2: partials are merged per (sequence, q head) by log-sum-exp.
+ *
+ *  q             bf16 [num_seqs][n_q_heads][head_dim]
+ *  block_table   int32 [num_seqs][max_blocks_per_seq]: page of each 16-token block
+ *  context_lens  int32 [num_seqs]: keys 0..ctx-1 are visible (the new token's K/V row
+ *                must already be written). Values are clamped on the device to
+ *                [0, min(max_context_len, 16*max_blocks_per_seq)]; a sequence with 0
+ *                keys produces zeros.
+ *  max_context_len   >= every context_lens[s] (sets the launch grid).
+ *  num_pages     pool size; a table entry outside [0, num_pages) reads page 0 instead
+ *                (memory-safe, result unspecified).
+ *  sm_scale      softmax scale, normally 1/sqrt(head_dim) = 1/16 [DCU §1.3].
+ *  out           fp32 [num_seqs][n_q_heads][head_dim], fully overwritten.
+ *  workspace     >= attn_decode_workspace_bytes(...) bytes, device memory, contents
+ *                undefined after the call. Calls sharing one workspace must be ordered
+ *                on one stream. */
+int attn_decode(const uint16_t* q,
+                const int8_t* k_cache, const int8_t* v_cache,
+                const float* k_scale, const float* v_scale,
+                const int32_t* block_table, int max_blocks_per_seq,
+                const int32_t* context_lens, int num_seqs, int max_context_len,
+                int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                float sm_scale, float* out,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_prefill_chunk -- n_new query tokens at the tail of one sequence, one pass.
+ * [DCU §3.2: INT8 Q with history and current INT8 K/V in one online-softmax pass, INT8
+ *  QK, INT8 PV; DCU §3.3 and §1.3: the V scale is folded into the softmax weight, the
+ *  weight is quantized per block with scale = block absmax / 127 and the block's int8
+ *  product is scaled back by it; QSA "Approach": one pass with an online softmax, no
+ *  split and no merge; DOT4 recthist: prefix keys unmasked, causal check only on the
+ *  tail.]
+ *
+ *  q             bf16 [n_new][n_q_heads][head_dim]; query t sits at position
+ *                context_len - n_new + t.
+ *  block_table   int32 [ceil(context_len/16)] pages of this sequence.
+ *  context_len   keys 0..context_len-1, including the n_new new rows (already written).
+ *  causal        1: query t sees keys 0 .. context_len-n_new+t; 0: all keys.
+ *  Weights P are carried as int8 codes per (query row, aligned 64-key block) with
+ *  scale = max_k(p_k * sV_k) / 127 and multiplied with the V codes on the int8 matrix
+ *  cores; the softmax denominator sums the unquantized weights.
+ *  out           fp32 [n_new][n_q_heads][head_dim], fully overwritten.
+ *  n_new == 0 is a no-op returning I8A_OK. */
+int attn_prefill_chunk(const uint16_t* q, int n_new,
+                       const int8_t* k_cache, const int8_t* v_cache,
+                       const float* k_scale, const float* v_scale,
+                       const int32_t* block_table, int context_len, int causal,
+                       int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                       float sm_scale, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INT8ATTN_H */

@@ -1,0 +1,208 @@
+"""Python binding of libint8attn.so (MI355X / gfx950 INT8-KV paged attention).
+
+Argument marshalling only: every step of the computation runs in the library's HIP
+kernels. torch tensors supply device memory and the current HIP stream; nothing here
+computes on the host and there is no fallback path: if the library is missing or a
+call fails, an exception is raised.
+
+The functions mirror the C ABI in include/int8attn.h (same names, same layout).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+__all__ = ["lib", "PagedCache", "alloc_cache", "kv_quant_write", "q_quant", "attn_decode",
+           "attn_decode_workspace_bytes", "attn_prefill_chunk", "Int8AttnError",
+           "HEAD_DIM", "PAGE", "PARTITION", "EXPORTED_SYMBOLS"]
+
+HEAD_DIM = 256
+PAGE = 16
+PARTITION = 512
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint8attn.so")
+EXPORTED_SYMBOLS = ("int8attn_last_error", "int8attn_version", "kv_quant_write", "q_quant",
+                    "attn_decode_workspace_bytes", "attn_decode", "attn_prefill_chunk")
+
+_c_void = ctypes.c_void_p
+_c_int = ctypes.c_int
+_c_size = ctypes.c_size_t
+_c_float = ctypes.c_float
+
+_SIGNATURES = {
+    "int8attn_last_error": (ctypes.c_char_p, []),
+    "int8attn_version": (_c_int, []),
+    "kv_quant_write": (_c_int, [_c_void, _c_void, _c_int, _c_int, _c_int, _c_int, _c_void,
+                                _c_void, _c_void, _c_void, _c_void, _c_int, _c_void]),
+    "q_quant": (_c_int, [_c_void, _c_int, _c_int, _c_void, _c_void, _c_void]),
+    "attn_decode_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
+    "attn_decode": (_c_int, [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void, _c_int,
+                             _c_void, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                             _c_void, _c_void, _c_size, _c_void]),
+    "attn_prefill_chunk": (_c_int, [_c_void, _c_int, _c_void, _c_void, _c_void, _c_void,
+                                    _c_void, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    _c_float, _c_void, _c_void]),
+}
+
+
+class Int8AttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"int8attn error {code}: {msg}")
+        self.code = code
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libint8attn.so (built in-tree by int8_kv_cache_amd.build)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m int8_kv_cache_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise Int8AttnError(rc, lib().int8attn_last_error().decode())
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, contiguous=True) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+@dataclasses.dataclass
+class PagedCache:
+    """The four device arrays of the paged INT8 cache (layout: include/int8attn.h)."""
+    k_cache: torch.Tensor   # int8 [num_pages * n_kv_heads * 4096]
+    v_cache: torch.Tensor   # int8 [num_pages * n_kv_heads * 4096]
+    k_scale: torch.Tensor   # fp32 [num_pages * n_kv_heads * 16]
+    v_scale: torch.Tensor   # fp32 [num_pages * n_kv_heads * 16]
+    num_pages: int
+    n_kv_heads: int
+
+    def __post_init__(self):
+        blk = self.num_pages * self.n_kv_heads
+        for t, n, dt in ((self.k_cache, blk * PAGE * HEAD_DIM, torch.int8),
+                         (self.v_cache, blk * PAGE * HEAD_DIM, torch.int8),
+                         (self.k_scale, blk * PAGE, torch.float32),
+                         (self.v_scale, blk * PAGE, torch.float32)):
+            if t.numel() != n or t.dtype != dt or not t.is_contiguous():
+                raise ValueError("cache arrays do not match num_pages / n_kv_heads")
+
+    def ptrs(self):
+        return (_dev(self.k_cache, "k_cache", torch.int8), _dev(self.v_cache, "v_cache", torch.int8),
+                _dev(self.k_scale, "k_scale", torch.float32),
+                _dev(self.v_scale, "v_scale", torch.float32))
+
+
+def alloc_cache(num_pages: int, n_kv_heads: int, device="cuda") -> PagedCache:
+    """Zero-filled paged cache of num_pages pages."""
+    n = num_pages * n_kv_heads
+    return PagedCache(torch.zeros(n * PAGE * HEAD_DIM, dtype=torch.int8, device=device),
+                      torch.zeros(n * PAGE * HEAD_DIM, dtype=torch.int8, device=device),
+                      torch.zeros(n * PAGE, dtype=torch.float32, device=device),
+                      torch.zeros(n * PAGE, dtype=torch.float32, device=device),
+                      num_pages, n_kv_heads)
+
+
+def kv_quant_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, cache,
+                   stream=None) -> None:
+    """Quantize K/V rows [T, Hkv, 256] (fp32 or bf16) into the paged cache at their slots."""
+    if k.dim() != 3 or k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("k and v must both be [T, Hkv, head_dim] of one dtype")
+    T, H, D = k.shape
+    dt = {torch.float32: 0, torch.bfloat16: 1}.get(k.dtype)
+    if dt is None:
+        raise TypeError("k/v must be float32 or bfloat16")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [T]")
+    if H != cache.n_kv_heads:
+        raise ValueError("k/v head count differs from the cache")
+    _check(lib().kv_quant_write(_dev(k, "k"), _dev(v, "v"), dt, T, H, D,
+                                _dev(slot_mapping, "slot_mapping", torch.int32), *cache.ptrs(),
+                                cache.num_pages, _stream(stream)))
+
+
+def q_quant(q: torch.Tensor, stream=None):
+    """bf16 rows [..., 256] -> (int8 codes [..., 256], fp32 scales [...])."""
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q must be bfloat16")
+    D = q.shape[-1]
+    rows = q.numel() // D
+    codes = torch.empty(q.shape, dtype=torch.int8, device=q.device)
+    scales = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    _check(lib().q_quant(_dev(q, "q"), rows, D, codes.data_ptr(), scales.data_ptr(),
+                         _stream(stream)))
+    return codes, scales
+
+
+def attn_decode_workspace_bytes(num_seqs: int, max_context_len: int, n_q_heads: int,
+                                head_dim: int = HEAD_DIM) -> int:
+    return int(lib().attn_decode_workspace_bytes(num_seqs, max_context_len, n_q_heads, head_dim))
+
+
+def attn_decode(q: torch.Tensor, cache, block_table: torch.Tensor, context_lens: torch.Tensor,
+                max_context_len: int, sm_scale: float | None = None, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode: q bf16 [S, Hq, 256] -> out fp32 [S, Hq, 256] over the paged INT8 cache."""
+    if q.dtype != torch.bfloat16 or q.dim() != 3:
+        raise TypeError("q must be bfloat16 [S, Hq, head_dim]")
+    S, Hq, D = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != S:
+        raise ValueError("block_table must be [S, max_blocks]")
+    if context_lens.shape != (S,):
+        raise ValueError("context_lens must be [S]")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
+    need = attn_decode_workspace_bytes(S, max_context_len, Hq, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    sm = float(sm_scale if sm_scale is not None else D ** -0.5)
+    _check(lib().attn_decode(_dev(q, "q"), *cache.ptrs(),
+                             _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+                             _dev(context_lens, "context_lens", torch.int32), S,
+                             int(max_context_len), cache.num_pages, Hq, cache.n_kv_heads, D, sm,
+                             _dev(out, "out", torch.float32), _dev(workspace, "workspace"),
+                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def attn_prefill_chunk(q: torch.Tensor, cache, block_table: torch.Tensor, context_len: int,
+                       causal: bool = True, sm_scale: float | None = None,
+                       out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Chunk: q bf16 [n_new, Hq, 256] at the tail of one sequence -> out fp32 [n_new, Hq, 256]."""
+    if q.dtype != torch.bfloat16 or q.dim() != 3:
+        raise TypeError("q must be bfloat16 [n_new, Hq, head_dim]")
+    n_new, Hq, D = q.shape
+    if block_table.dim() != 1 or block_table.numel() < (context_len + PAGE - 1) // PAGE:
+        raise ValueError("block_table must be [ceil(context_len/16)]")
+    if out is None:
+        out = torch.empty((n_new, Hq, D), dtype=torch.float32, device=q.device)
+    sm = float(sm_scale if sm_scale is not None else D ** -0.5)
+    _check(lib().attn_prefill_chunk(_dev(q, "q"), n_new, *cache.ptrs(),
+                                    _dev(block_table, "block_table", torch.int32),
+                                    int(context_len), int(bool(causal)), cache.num_pages, Hq,
+                                    cache.n_kv_heads, D, sm,
+                                    _dev(out, "out", torch.float32), _stream(stream)))
+    return out

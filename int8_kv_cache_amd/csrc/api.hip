@@ -1,0 +1,140 @@
+// extern "C" entry points: argument validation, workspace sizing, launch, error codes.
+// Nothing here allocates or synchronizes; every check happens before anything is
+// enqueued, so an error leaves every output untouched.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "int8attn.h"
+#include "launch.hpp"
+
+namespace i8a {
+
+static thread_local std::string g_last_error;
+
+int set_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(I8A_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return I8A_OK;
+}
+
+static int check_heads(int n_q_heads, int n_kv_heads, int head_dim) {
+  if (n_q_heads <= 0 || n_kv_heads <= 0) return set_error(I8A_EINVAL, "head counts must be > 0");
+  if (n_kv_heads > 65535) return set_error(I8A_EINVAL, "n_kv_heads > 65535");
+  if (head_dim != 256) return set_error(I8A_EUNSUPPORTED, "head_dim %d unsupported (v1: 256)", head_dim);
+  if (n_q_heads != 6 * n_kv_heads)
+    return set_error(I8A_EUNSUPPORTED, "n_q_heads %d / n_kv_heads %d: v1 supports GQA groups of 6",
+                     n_q_heads, n_kv_heads);
+  return I8A_OK;
+}
+
+static size_t decode_ws_bytes(long long num_seqs, long long max_ctx, long long n_q_heads) {
+  const long long parts = (max_ctx + 511) / 512;
+  const long long floats = num_seqs * n_q_heads * parts * (2 + 256);
+  return (size_t)((floats * 4 + 255) / 256 * 256);
+}
+
+}  // namespace i8a
+
+using namespace i8a;
+
+extern "C" {
+
+const char* int8attn_last_error(void) { return g_last_error.c_str(); }
+
+int int8attn_version(void) { return (1 << 16) | 0; }
+
+int kv_quant_write(const void* k, const void* v, int in_dtype, int n_tokens, int n_kv_heads,
+                   int head_dim, const int32_t* slot_mapping, int8_t* k_cache, int8_t* v_cache,
+                   float* k_scale, float* v_scale, int num_pages, void* stream) {
+  if (in_dtype != I8A_DTYPE_F32 && in_dtype != I8A_DTYPE_BF16)
+    return set_error(I8A_EINVAL, "kv_quant_write: in_dtype %d", in_dtype);
+  if (n_tokens < 0 || n_kv_heads <= 0 || num_pages <= 0)
+    return set_error(I8A_EINVAL, "kv_quant_write: n_tokens %d, n_kv_heads %d, num_pages %d",
+                     n_tokens, n_kv_heads, num_pages);
+  if (head_dim != 256)
+    return set_error(I8A_EUNSUPPORTED, "kv_quant_write: head_dim %d unsupported (v1: 256)", head_dim);
+  if ((long long)n_tokens * n_kv_heads > 2147483000LL)
+    return set_error(I8A_EINVAL, "kv_quant_write: too many rows");
+  if (n_tokens == 0) return I8A_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
+    return set_error(I8A_EINVAL, "kv_quant_write: null pointer");
+  return launch_kv_quant_write(k, v, in_dtype == I8A_DTYPE_BF16, n_tokens, n_kv_heads,
+                               slot_mapping, k_cache, v_cache, k_scale, v_scale, num_pages,
+                               (hipStream_t)stream);
+}
+
+int q_quant(const uint16_t* q_bf16, int n_rows, int head_dim, int8_t* codes, float* scales,
+            void* stream) {
+  if (n_rows < 0 || n_rows > 2147483000) return set_error(I8A_EINVAL, "q_quant: n_rows %d", n_rows);
+  if (head_dim != 256) return set_error(I8A_EUNSUPPORTED, "q_quant: head_dim %d unsupported", head_dim);
+  if (n_rows == 0) return I8A_OK;
+  if (!q_bf16 || !codes || !scales) return set_error(I8A_EINVAL, "q_quant: null pointer");
+  return launch_q_quant(q_bf16, n_rows, codes, scales, (hipStream_t)stream);
+}
+
+size_t attn_decode_workspace_bytes(int num_seqs, int max_context_len, int n_q_heads, int head_dim) {
+  if (num_seqs <= 0 || max_context_len <= 0 || n_q_heads <= 0 || head_dim != 256) return 0;
+  return decode_ws_bytes(num_seqs, max_context_len, n_q_heads);
+}
+
+int attn_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cache,
+                const float* k_scale, const float* v_scale, const int32_t* block_table,
+                int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                int max_context_len, int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
+  if (rc) return rc;
+  if (num_seqs < 0 || num_seqs > 65535) return set_error(I8A_EINVAL, "attn_decode: num_seqs %d", num_seqs);
+  if (num_seqs == 0) return I8A_OK;
+  if (max_context_len <= 0 || max_blocks_per_seq <= 0 || num_pages <= 0)
+    return set_error(I8A_EINVAL, "attn_decode: max_context_len %d, max_blocks_per_seq %d, num_pages %d",
+                     max_context_len, max_blocks_per_seq, num_pages);
+  if (!isfinite(sm_scale)) return set_error(I8A_EINVAL, "attn_decode: sm_scale not finite");
+  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_table || !context_lens || !out ||
+      !workspace)
+    return set_error(I8A_EINVAL, "attn_decode: null pointer");
+  if (((uintptr_t)workspace & 15u) != 0) return set_error(I8A_EINVAL, "attn_decode: workspace not 16-byte aligned");
+  const size_t need = decode_ws_bytes(num_seqs, max_context_len, n_q_heads);
+  if (workspace_bytes < need)
+    return set_error(I8A_EWORKSPACE, "attn_decode: workspace %zu bytes < %zu needed", workspace_bytes, need);
+  const int max_parts = (max_context_len + 511) / 512;
+  return launch_decode(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks_per_seq,
+                       context_lens, num_seqs, max_context_len, num_pages, n_q_heads, n_kv_heads,
+                       sm_scale, out, (float*)workspace, max_parts, (hipStream_t)stream);
+}
+
+int attn_prefill_chunk(const uint16_t* q, int n_new, const int8_t* k_cache, const int8_t* v_cache,
+                       const float* k_scale, const float* v_scale, const int32_t* block_table,
+                       int context_len, int causal, int num_pages, int n_q_heads, int n_kv_heads,
+                       int head_dim, float sm_scale, float* out, void* stream) {
+  int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
+  if (rc) return rc;
+  if (n_new < 0 || context_len < 1 || n_new > context_len || num_pages <= 0 ||
+      (causal != 0 && causal != 1))
+    return set_error(I8A_EINVAL, "attn_prefill_chunk: n_new %d, context_len %d, num_pages %d, causal %d",
+                     n_new, context_len, num_pages, causal);
+  if (context_len > 2147483000 - 64) return set_error(I8A_EINVAL, "attn_prefill_chunk: context too long");
+  if (!isfinite(sm_scale)) return set_error(I8A_EINVAL, "attn_prefill_chunk: sm_scale not finite");
+  if (n_new == 0) return I8A_OK;
+  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_table || !out)
+    return set_error(I8A_EINVAL, "attn_prefill_chunk: null pointer");
+  return launch_prefill(q, n_new, k_cache, v_cache, k_scale, v_scale, block_table, context_len,
+                        causal, num_pages, n_q_heads, n_kv_heads, sm_scale, out,
+                        (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Device helpers shared by the gfx950 kernels of the INT8-KV attention library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8a {
+
+constexpr int kHeadDim = 256;
+constexpr int kPage = 16;          // tokens per page
+constexpr int kBlockBytes = 4096;  // codes per (page, kv head)
+constexpr int kGroup = 6;          // query heads per KV head (v1 contract)
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Max / sum over all 64 lanes of a wave, result in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Reductions over the 4 lanes {n, n+16, n+32, n+48} that share one column of a
+// 16x16 matrix-core accumulator (the column index is lane % 16).
+__device__ __forceinline__ float col_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float col_sum(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// Row quantizer for one row of 256 values spread over a wave, 4 per lane (lane l holds
+// elements 4l..4l+3). Rule: amax = max|x|, scale = amax/127 (IEEE fp32 division),
+// code = clamp(rint(x/scale), -127, 127) with x/scale an IEEE division and rint half
+// to even; scale == 0 gives all-zero codes. Returns the 4 codes packed little-endian.
+// ("INT8 KV and INT8 MMAC attention on a gfx936 DCU", §2.1.)
+__device__ __forceinline__ uint32_t quantize4(float x0, float x1, float x2, float x3,
+                                              float* scale_out) {
+  float a = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
+  const float amax = wave_max(a);
+  const float scale = amax / 127.0f;
+  *scale_out = scale;
+  if (scale == 0.0f) return 0u;
+  auto q = [scale](float x) -> uint32_t {
+    float r = rintf(x / scale);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (uint32_t)((int)r) & 0xffu;
+  };
+  return q(x0) | (q(x1) << 8) | (q(x2) << 16) | (q(x3) << 24);
+}
+
+// Four signed int8 codes (one dword) -> their exact values as fp16, in two halves of
+// two. 1024 + (b + 128) is exact in fp16; subtracting 1152 leaves b.
+__device__ __forceinline__ void i8x4_to_f16(uint32_t a, h2* lo, h2* hi) {
+  const uint32_t u = a ^ 0x80808080u;
+  const uint32_t p0 = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t p1 = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  *lo = __builtin_bit_cast(h2, p0) - bias;
+  *hi = __builtin_bit_cast(h2, p1) - bias;
+}
+
+__device__ __forceinline__ v8h i8x8_to_f16(uint32_t a0, uint32_t a1) {
+  h2 r0, r1, r2, r3;
+  i8x4_to_f16(a0, &r0, &r1);
+  i8x4_to_f16(a1, &r2, &r3);
+  v8h o;
+  o[0] = r0[0]; o[1] = r0[1]; o[2] = r1[0]; o[3] = r1[1];
+  o[4] = r2[0]; o[5] = r2[1]; o[6] = r3[0]; o[7] = r3[1];
+  return o;
+}
+
+}  // namespace i8a

@@ -1,0 +1,29 @@
+// Host-side launch helpers and error plumbing shared by the kernel files and api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8a {
+
+// Records a thread-local message for int8attn_last_error() and returns `code`.
+int set_error(int code, const char* fmt, ...);
+// hipGetLastError() after a launch: I8A_OK or I8A_ELAUNCH with the runtime's message.
+int check_launch(const char* what);
+
+int launch_kv_quant_write(const void* k, const void* v, int in_bf16, int n_tokens, int n_kv_heads,
+                          const int32_t* slots, int8_t* k_cache, int8_t* v_cache, float* k_scale,
+                          float* v_scale, int num_pages, hipStream_t stream);
+int launch_q_quant(const uint16_t* q, int n_rows, int8_t* codes, float* scales,
+                   hipStream_t stream);
+int launch_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cache,
+                  const float* k_scale, const float* v_scale, const int32_t* block_table,
+                  int max_blocks, const int32_t* ctx_lens, int num_seqs, int max_ctx,
+                  int num_pages, int n_q_heads, int n_kv_heads, float sm_scale, float* out,
+                  float* ws, int max_parts, hipStream_t stream);
+int launch_prefill(const uint16_t* q, int n_new, const int8_t* k_cache, const int8_t* v_cache,
+                   const float* k_scale, const float* v_scale, const int32_t* block_table,
+                   int ctx, int causal, int num_pages, int n_q_heads, int n_kv_heads,
+                   float sm_scale, float* out, hipStream_t stream);
+
+}  // namespace i8a

@@ -1,0 +1,110 @@
+"""kv_quant_write and q_quant against the oracle: codes and scales bit-exact, cache bytes
+outside the written slots untouched ("INT8 KV and INT8 MMAC attention on a gfx936 DCU"
+§2.1 rule, §2.3 paged layout)."""
+import numpy as np
+import pytest
+import torch
+
+import int8_kv_cache_amd as lib
+import workloads
+from oracle import paged, quant
+from tests.gpu_support import (bf16_tensor, cache_to_host, gpu_cache, need_gpu, oracle_cache,
+                               say, up)
+
+pytestmark = pytest.mark.gpu
+
+
+def _write_and_compare(k, v, slots, num_pages, H, in_bf16=False):
+    cache = gpu_cache(num_pages, H)
+    if in_bf16:
+        kt = bf16_tensor(workloads.f32_to_bf16_bits(k)); vt = bf16_tensor(workloads.f32_to_bf16_bits(v))
+        k = quant.bf16_bits_to_f32(workloads.f32_to_bf16_bits(k))
+        v = quant.bf16_bits_to_f32(workloads.f32_to_bf16_bits(v))
+    else:
+        kt, vt = up(k), up(v)
+    lib.kv_quant_write(kt, vt, up(slots.astype(np.int32)), cache)
+    got = cache_to_host(cache)
+    ref = oracle_cache(num_pages, H)
+    kc, ks = quant.quantize_rows(k); vc, vs = quant.quantize_rows(v)
+    paged.write_rows(ref, slots, kc, ks, vc, vs)
+    names = ("k_cache", "v_cache", "k_scale", "v_scale")
+    for name, a, b in zip(names, got, ref):
+        if a.dtype == np.float32:
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), name
+        else:
+            assert np.array_equal(a, b), name
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_config_rows_bit_exact(cfg):
+    need_gpu()
+    case = workloads.config_case(cfg)
+    say(f"kv_quant_write config {cfg}")
+    if cfg == 4:
+        k, v, _, slots = case.data()
+    else:
+        k, v, _, slots = case.all_data()
+    _write_and_compare(k, v, slots, case.num_pages, case.n_kv_heads)
+
+
+def test_near_ties_zero_rows_and_extremes():
+    need_gpu()
+    rows = workloads.near_tie_rows(3, 4 * 300)
+    rng = np.random.default_rng(4)
+    rows[:8] = 0.0                                   # amax = 0
+    rows[8, :] = 0.0; rows[8, 5] = 1e-45             # scale underflows to 0
+    rows[9] = rng.standard_normal(256).astype(np.float32) * np.float32(1e-38)  # denormal-ish scale
+    rows[10] = rng.standard_normal(256).astype(np.float32) * np.float32(1e30)
+    k = rows.reshape(300, 4, 256)
+    v = rows[::-1].copy().reshape(300, 4, 256)
+    slots = rng.permutation(40 * 16)[:300].astype(np.int32)
+    _write_and_compare(k, v, slots, 40, 4)
+
+
+def test_bf16_input_and_skipped_slots():
+    need_gpu()
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((70, 4, 256)).astype(np.float32) * 3
+    v = rng.standard_normal((70, 4, 256)).astype(np.float32)
+    slots = rng.permutation(10 * 16)[:70].astype(np.int32)
+    slots[[3, 10]] = -1                               # skipped
+    slots[[20]] = 10 * 16 + 5                         # past the pool: skipped
+    ref_slots = slots.copy(); ref_slots[20] = -1
+    cache = gpu_cache(10, 4)
+    kt = bf16_tensor(workloads.f32_to_bf16_bits(k)); vt = bf16_tensor(workloads.f32_to_bf16_bits(v))
+    lib.kv_quant_write(kt, vt, up(slots), cache)
+    got = cache_to_host(cache)
+    ref = oracle_cache(10, 4)
+    kf = quant.bf16_bits_to_f32(workloads.f32_to_bf16_bits(k))
+    vf = quant.bf16_bits_to_f32(workloads.f32_to_bf16_bits(v))
+    kc, ks = quant.quantize_rows(kf); vc, vs = quant.quantize_rows(vf)
+    paged.write_rows(ref, ref_slots, kc, ks, vc, vs)
+    for a, b in zip(got, ref):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_other_head_counts():
+    need_gpu()
+    rng = np.random.default_rng(6)
+    for H in (1, 3, 8):
+        k = rng.standard_normal((33, H, 256)).astype(np.float32)
+        v = rng.standard_normal((33, H, 256)).astype(np.float32)
+        slots = rng.permutation(4 * 16)[:33].astype(np.int32)
+        _write_and_compare(k, v, slots, 4, H)
+
+
+def test_q_quant_bit_exact():
+    need_gpu()
+    case = workloads.config_case(4)
+    _, _, q, _ = case.data()
+    q = q[:512]
+    codes, scales = lib.q_quant(bf16_tensor(q))
+    torch.cuda.synchronize()
+    rc, rs = quant.quantize_rows(quant.bf16_bits_to_f32(q))
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    ties = workloads.f32_to_bf16_bits(workloads.near_tie_rows(9, 200))
+    codes, scales = lib.q_quant(bf16_tensor(ties))
+    rc, rs = quant.quantize_rows(quant.bf16_bits_to_f32(ties))
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))

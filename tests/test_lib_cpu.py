@@ -1,0 +1,135 @@
+"""The C-ABI library loads and exports every symbol the header declares; host-side
+argument validation returns the documented error codes without enqueuing anything
+(no GPU is touched: every call below fails validation before any HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import int8_kv_cache_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "int8attn.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def _codes():
+    src = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"#define\s+(I8A_\w+)\s+(-?\d+)", src)}
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared_functions() == sorted(m.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = m.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(_declared_functions()) <= exported
+
+
+def test_version():
+    assert m.lib().int8attn_version() >> 16 == 1
+
+
+FAKE = 0x1000  # never dereferenced: every call below is rejected on the host
+
+
+def _err(rc):
+    return rc, m.lib().int8attn_last_error().decode()
+
+
+def test_kv_quant_write_validation():
+    C = _codes()
+    L = m.lib()
+    args = dict(k=FAKE, v=FAKE, dt=0, T=4, H=4, D=256, slots=FAKE, kc=FAKE, vc=FAKE, ks=FAKE,
+                vs=FAKE, P=8, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return _err(L.kv_quant_write(a["k"], a["v"], a["dt"], a["T"], a["H"], a["D"], a["slots"],
+                                     a["kc"], a["vc"], a["ks"], a["vs"], a["P"], a["s"]))
+
+    assert call(dt=7)[0] == C["I8A_EINVAL"]
+    assert call(D=128)[0] == C["I8A_EUNSUPPORTED"]
+    assert call(T=-1)[0] == C["I8A_EINVAL"]
+    assert call(P=0)[0] == C["I8A_EINVAL"]
+    rc, msg = call(k=None)
+    assert rc == C["I8A_EINVAL"] and "null" in msg
+    assert call(T=0)[0] == C["I8A_OK"]          # empty input: no-op
+
+
+def test_q_quant_validation():
+    C = _codes()
+    L = m.lib()
+    assert L.q_quant(FAKE, 3, 64, FAKE, FAKE, None) == C["I8A_EUNSUPPORTED"]
+    assert L.q_quant(None, 3, 256, FAKE, FAKE, None) == C["I8A_EINVAL"]
+    assert L.q_quant(FAKE, 0, 256, FAKE, FAKE, None) == C["I8A_OK"]
+
+
+def test_workspace_bytes_formula():
+    L = m.lib()
+    # num_seqs * n_q_heads * ceil(ctx/512) * (2 + 256) floats, rounded up to 256 bytes
+    assert L.attn_decode_workspace_bytes(1, 32768, 24, 256) == 24 * 64 * 258 * 4
+    assert L.attn_decode_workspace_bytes(3, 513, 24, 256) == ((3 * 24 * 2 * 258 * 4 + 255) // 256) * 256
+    assert L.attn_decode_workspace_bytes(0, 512, 24, 256) == 0
+    assert L.attn_decode_workspace_bytes(1, 512, 24, 128) == 0
+
+
+def test_attn_decode_validation():
+    C = _codes()
+    L = m.lib()
+    base = [FAKE] * 6 + [16, FAKE, 1, 256, 16, 24, 4, 256, 0.0625, FAKE, FAKE, 10 ** 7, None]
+
+    def call(i=None, val=None):
+        a = list(base)
+        if i is not None:
+            a[i] = val
+        return L.attn_decode(*a)
+
+    assert call(12, 8) == C["I8A_EUNSUPPORTED"]        # 24 q heads over 8 kv heads
+    assert call(13, 128) == C["I8A_EUNSUPPORTED"]      # head_dim
+    assert call(9, 0) == C["I8A_EINVAL"]               # max_context_len
+    assert call(10, 0) == C["I8A_EINVAL"]              # num_pages
+    assert call(14, float("nan")) == C["I8A_EINVAL"]   # sm_scale
+    assert call(0, None) == C["I8A_EINVAL"]            # q null
+    assert call(17, 100) == C["I8A_EWORKSPACE"]
+    assert call(16, FAKE + 4) == C["I8A_EINVAL"]       # misaligned workspace
+    assert call(8, 0) == C["I8A_OK"]                   # no sequences: no-op
+
+
+def test_attn_prefill_validation():
+    C = _codes()
+    L = m.lib()
+    base = [FAKE, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 1, 16, 24, 4, 256, 0.0625, FAKE, None]
+
+    def call(i=None, val=None):
+        a = list(base)
+        if i is not None:
+            a[i] = val
+        return L.attn_prefill_chunk(*a)
+
+    assert call(10, 12) == C["I8A_EUNSUPPORTED"]
+    assert call(1, 101) == C["I8A_EINVAL"]             # n_new > context_len
+    assert call(8, 2) == C["I8A_EINVAL"]               # causal flag
+    assert call(7, 0) == C["I8A_EINVAL"]               # empty context
+    assert call(14, None) == C["I8A_EINVAL"]           # out null
+    assert call(1, 0) == C["I8A_OK"]                   # no queries: no-op
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        m.q_quant(torch.zeros(2, 256, dtype=torch.bfloat16))
