@@ -58,13 +58,14 @@ def attention_exact(qd, kd, vd, sm_scale, last_key, *, row_chunk=128, return_sta
         for r0 in range(0, R, row_chunk):
             r1 = min(R, r0 + row_chunk)
             qg = qd[r0:r1, heads, :]                               # [r, group, D]
-            s = np.einsum("rhd,nd->rhn", qg, kg) * sm_scale        # [r, group, N]
+            r = r1 - r0
+            s = (qg.reshape(r * group, D) @ kg.T).reshape(r, group, N) * sm_scale
             vis = key_idx[None, :] <= last_key[r0:r1, None]        # [r, N]
             s = np.where(vis[:, None, :], s, -np.inf)
             m = s.max(axis=-1)
             p = np.exp(s - m[..., None])
             l = p.sum(axis=-1)
-            out[r0:r1, heads, :] = np.einsum("rhn,nd->rhd", p, vg) / l[..., None]
+            out[r0:r1, heads, :] = (p.reshape(r * group, N) @ vg).reshape(r, group, D) / l[..., None]
             m_all[r0:r1, heads] = m; l_all[r0:r1, heads] = l
     if return_stats:
         return out, m_all, l_all
@@ -128,7 +129,8 @@ def attention_int8p(qd, kd, v_codes, v_scales, sm_scale, last_key, *, block=64, 
         vsg = vs[:, g]
         for r0 in range(0, R, row_chunk):
             r1 = min(R, r0 + row_chunk)
-            s = np.einsum("rhd,nd->rhn", qd[r0:r1, heads, :], kd[:, g, :]) * sm_scale
+            r = r1 - r0
+            s = (qd[r0:r1, heads, :].reshape(r * group, D) @ kd[:, g, :].T).reshape(r, group, N) * sm_scale
             vis = key_idx[None, :] <= last_key[r0:r1, None]
             s = np.where(vis[:, None, :], s, -np.inf)
             m = s.max(axis=-1, keepdims=True)
@@ -140,7 +142,8 @@ def attention_int8p(qd, kd, v_codes, v_scales, sm_scale, last_key, *, block=64, 
             sb = w.max(axis=-1) / 127.0                          # [r, group, nb]
             safe = np.where(sb > 0, sb, 1.0)
             c = np.where(sb[..., None] > 0, np.rint(w / safe[..., None]), 0.0)
-            acc = np.einsum("rhbk,bkd->rhbd", c, vcg)            # exact integer sums
+            acc = np.matmul(c.transpose(2, 0, 1, 3).reshape(nb, r * group, block), vcg)
+            acc = acc.reshape(nb, r, group, D).transpose(1, 2, 0, 3)   # exact integer sums
             out[r0:r1, heads, :] = (acc * sb[..., None]).sum(axis=2) / l[..., None]
     return out
 
