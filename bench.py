@@ -1,0 +1,240 @@
+"""Benchmark of the INT8-KV attention hot path on one MI355X.
+
+One step = every row of the path over one batch of synthetic input:
+  1. kv_quant_write of the 2048 new rows of a causal prefill chunk (fp32 K/V in);
+  2. attn_prefill_chunk: 2048 queries at the tail of a 32768-key context
+     (30720 cached + 2048 new), 24 q / 4 KV heads, head_dim 256, int8 P per 64-key block;
+  3. kv_quant_write of one new decode token;
+  4. attn_decode at context 32768 (split-K over 64 partitions of 512 rows + merge).
+The decode reads one of `--decode-copies` identical caches per step, in rotation, so
+its 68 MB working set is not served from the 256 MB Infinity Cache (MALL-cold).
+
+Printed: one JSON line. `value` is attn_decode microseconds per call at ctx 32768
+(the headline of the metric); decode HBM GB/s, prefill int8 TOPS and MFMA utilisation,
+quant-write GB/s and the per-step wall time are extra fields. Per-kernel times are HIP
+events on the stream the library launches on, averaged over the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+import workloads
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
+
+
+def decode_bytes(ctx: int, n_q_heads: int, n_kv_heads: int, D: int) -> int:
+    """Algorithmic bytes of one decode call: every K/V code and scale of the context,
+    the block table, the query, the output and the context length."""
+    per_token = n_kv_heads * (2 * D + 2 * 4)
+    pages = -(-ctx // workloads.PAGE)
+    return ctx * per_token + pages * 4 + n_q_heads * D * 2 + n_q_heads * D * 4 + 4
+
+
+def prefill_ops(ctx: int, n_new: int, n_q_heads: int, D: int) -> int:
+    """int8 ops of one causal chunk: visible (query, key) pairs x heads x (QK + PV) MACs x 2."""
+    pos0 = ctx - n_new
+    pairs = n_new * pos0 + n_new * (n_new + 1) // 2
+    return pairs * n_q_heads * 4 * D
+
+
+def quant_write_bytes(n_tokens: int, n_kv_heads: int, D: int) -> int:
+    """fp32 K and V rows in + slot index + int8 codes and fp32 scales out."""
+    return n_tokens * (2 * n_kv_heads * D * 4 + 4 + n_kv_heads * (2 * D + 8))
+
+
+def cpu_baseline(dec_case, dec_data, pf_case, pf_data, budget_s=20.0):
+    """The oracle, unchanged, on the host: decode at ctx 32768 (whole calls) and a
+    sample of prefill query rows of the same chunk; quantization excluded."""
+    from oracle import attention, quant
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    k, v, q, _ = dec_data
+    kc, ks = quant.quantize_rows(k); vc, vs = quant.quantize_rows(v)
+    qc, qs = quant.quantize_rows(quant.bf16_bits_to_f32(q[0, 0]))
+    view = (kc, ks, vc, vs)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        attention.decode_exact(qc, qs, view, workloads.SM_SCALE)
+        calls += 1
+        if time.perf_counter() - t0 > budget_s / 2 or calls >= 20:
+            break
+    dec_us = (time.perf_counter() - t0) / calls * 1e6
+
+    k4, v4, q4, _ = pf_data
+    kc4, ks4 = quant.quantize_rows(k4); vc4, vs4 = quant.quantize_rows(v4)
+    kd, vd = quant.dequantize(kc4, ks4), quant.dequantize(vc4, vs4)
+    pos0 = pf_case.context_len - pf_case.n_new
+    rows_done, ops, t0 = 0, 0, time.perf_counter()
+    rng = np.random.default_rng(0)
+    while time.perf_counter() - t0 < budget_s / 2 and rows_done < pf_case.n_new:
+        rows = np.sort(rng.choice(pf_case.n_new, 16, replace=False))
+        qcr, qsr = quant.quantize_rows(quant.bf16_bits_to_f32(q4[rows]))
+        attention.attention_exact(quant.dequantize(qcr, qsr), kd, vd, workloads.SM_SCALE,
+                                  pos0 + rows)
+        rows_done += len(rows)
+        ops += int(np.sum(pos0 + rows + 1)) * pf_case.n_q_heads * 4 * pf_case.head_dim
+    pf_tops = ops / (time.perf_counter() - t0) / 1e12
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "decode": {"value": round(dec_us, 1), "unit": "us/call", "cores": blas_threads or cores,
+                   "kind": "oracle", "host_cores": cores,
+                   "sample": f"{calls} full decode calls at ctx 32768 (24 q heads), from codes"},
+        "prefill": {"value": round(pf_tops, 6), "unit": "TOPS (int8-equivalent ops/s)",
+                    "cores": blas_threads or cores, "kind": "oracle", "host_cores": cores,
+                    "sample": f"{rows_done} of 2048 query tokens (all 24 heads) of the chunk"},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-copies", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build measures the single-GPU path "
+              "(see DESIGN.md for how it would shard); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int8_kv_cache_amd as lib
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def bf16(bits):
+        return up(bits.view(np.int16)).view(torch.bfloat16)
+
+    # ---- decode workload: config 3 (ctx 32768, 1 sequence, random pages)
+    dec = workloads.config_case(3)
+    dec_data = dec.all_data()
+    k, v, q, slots = dec_data
+    ctx = dec.max_context_len
+    base = lib.alloc_cache(dec.num_pages, dec.n_kv_heads, dev)
+    lib.kv_quant_write(up(k), up(v), up(slots), base)
+    copies = [base] + [lib.PagedCache(base.k_cache.clone(), base.v_cache.clone(),
+                                      base.k_scale.clone(), base.v_scale.clone(),
+                                      base.num_pages, base.n_kv_heads)
+                       for _ in range(args.decode_copies - 1)]
+    q_dec = bf16(q[:, 0])                                   # [1, 24, 256]
+    table = up(dec.block_table)
+    ctx_t = up(dec.context_lens)
+    k_new, v_new, slot_new = up(k[-1:]), up(v[-1:]), up(slots[-1:])
+    out_dec = torch.empty((1, dec.n_q_heads, dec.head_dim), dtype=torch.float32, device=dev)
+    ws = torch.empty(lib.attn_decode_workspace_bytes(1, ctx, dec.n_q_heads), dtype=torch.uint8,
+                     device=dev)
+
+    # ---- prefill workload: config 4 (2048 new queries at ctx 32768, causal)
+    pf = workloads.config_case(4)
+    pf_data = pf.data()
+    k4, v4, q4, slots4 = pf_data
+    pos0 = pf.context_len - pf.n_new
+    pcache = lib.alloc_cache(pf.num_pages, pf.n_kv_heads, dev)
+    lib.kv_quant_write(up(k4[:pos0]), up(v4[:pos0]), up(slots4[:pos0]), pcache)
+    k_chunk, v_chunk, s_chunk = up(k4[pos0:]), up(v4[pos0:]), up(slots4[pos0:])
+    q_pf = bf16(q4)
+    ptable = up(pf.block_table)
+    out_pf = torch.empty((pf.n_new, pf.n_q_heads, pf.head_dim), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    n_ev = 5
+    steps_total = args.warmup + args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps_total)]
+
+    def step(i):
+        ev = events[i]
+        c = copies[i % len(copies)]
+        ev[0].record()
+        lib.kv_quant_write(k_chunk, v_chunk, s_chunk, pcache)
+        ev[1].record()
+        lib.attn_prefill_chunk(q_pf, pcache, ptable, pf.context_len, True, out=out_pf)
+        ev[2].record()
+        lib.kv_quant_write(k_new, v_new, slot_new, c)
+        ev[3].record()
+        lib.attn_decode(q_dec, c, table, ctx_t, ctx, out=out_dec, workspace=ws)
+        ev[4].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, steps_total):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def mean_ms(a, b):
+        return float(np.mean([events[i][a].elapsed_time(events[i][b])
+                              for i in range(args.warmup, steps_total)]))
+
+    qw_chunk_ms, pf_ms, qw_tok_ms, dec_ms = (mean_ms(0, 1), mean_ms(1, 2), mean_ms(2, 3),
+                                             mean_ms(3, 4))
+    dec_b = decode_bytes(ctx, dec.n_q_heads, dec.n_kv_heads, dec.head_dim)
+    pf_ops = prefill_ops(pf.context_len, pf.n_new, pf.n_q_heads, pf.head_dim)
+    qw_b = quant_write_bytes(pf.n_new, pf.n_kv_heads, pf.head_dim)
+    dec_gbps = dec_b / (dec_ms * 1e-3) / 1e9
+    pf_tops = pf_ops / (pf_ms * 1e-3) / 1e12
+    qw_gbps = qw_b / (qw_chunk_ms * 1e-3) / 1e9
+
+    res = {
+        "metric": "decode attn us/call + HBM GB/s at 32k ctx; prefill-chunk int8 TOPS (MFMA util)",
+        "value": round(dec_ms * 1e3, 3),
+        "unit": "us/call",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic (seeded N(0,1) K/V/Q, K outlier channels x10 in the chunk; random page tables)",
+        "config": {"workload": "decode ctx=32768 (1 seq, 24q/4kv, d256, 64 partitions of 512, "
+                               "MALL-cold over %d cache copies) + causal prefill chunk 2048 q at "
+                               "ctx=32768 (30720 cached) + kv_quant_write of 2048+1 rows"
+                               % len(copies),
+                   "decode_ctx": ctx, "prefill_ctx": pf.context_len, "prefill_n_new": pf.n_new,
+                   "n_q_heads": 24, "n_kv_heads": 4, "head_dim": 256, "page": 16,
+                   "partition": 512},
+        "decode_us": round(dec_ms * 1e3, 3),
+        "decode_hbm_GBps": round(dec_gbps, 1),
+        "prefill_ms": round(pf_ms, 4),
+        "prefill_int8_TOPS": round(pf_tops, 1),
+        "prefill_mfma_util": round(pf_tops / INT8_PEAK_TOPS, 4),
+        "quant_write_2048_us": round(qw_chunk_ms * 1e3, 3),
+        "quant_write_GBps": round(qw_gbps, 1),
+        "quant_write_1tok_us": round(qw_tok_ms * 1e3, 3),
+        "roofline": {"bound": "mfma", "kernel": "prefill_chunk_kernel",
+                     "achieved": round(pf_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
+                     "frac": round(pf_tops / INT8_PEAK_TOPS, 4),
+                     "per_launch": pf_ops, "traffic": None},
+        "roofline_decode": {"bound": "hbm", "kernel": "attn_decode (split + merge)",
+                            "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "per_launch": dec_b,
+                            "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(dec, dec_data, pf, pf_data, args.cpu_budget)
+        res["cpu_baseline"] = cb["decode"]
+        res["cpu_baseline_prefill"] = cb["prefill"]
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
