@@ -15,6 +15,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
@@ -60,20 +61,22 @@ __device__ __forceinline__ uint32_t quantize4(float x0, float x1, float x2, floa
 }
 
 // Four signed int8 codes (one dword) -> their exact values as fp16, in two halves of
-// two. 1024 + (b + 128) is exact in fp16; subtracting 1152 leaves b.
-__device__ __forceinline__ void i8x4_to_f16(uint32_t a, h2* lo, h2* hi) {
-  const uint32_t u = a ^ 0x80808080u;
+// two. 1024 + (b + 128) is exact in fp16; subtracting 1152 leaves b. `bias` must be
+// 0x80808080 (it is a parameter so that a caller can pass it through memory and keep
+// the conversion from being scheduled ahead of a barrier).
+__device__ __forceinline__ void i8x4_to_f16(uint32_t a, h2* lo, h2* hi, uint32_t bias) {
+  const uint32_t u = a ^ bias;
   const uint32_t p0 = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
   const uint32_t p1 = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
-  const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  *lo = __builtin_bit_cast(h2, p0) - bias;
-  *hi = __builtin_bit_cast(h2, p1) - bias;
+  const h2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  *lo = __builtin_bit_cast(h2, p0) - off;
+  *hi = __builtin_bit_cast(h2, p1) - off;
 }
 
-__device__ __forceinline__ v8h i8x8_to_f16(uint32_t a0, uint32_t a1) {
+__device__ __forceinline__ v8h i8x8_to_f16(uint32_t a0, uint32_t a1, uint32_t bias) {
   h2 r0, r1, r2, r3;
-  i8x4_to_f16(a0, &r0, &r1);
-  i8x4_to_f16(a1, &r2, &r3);
+  i8x4_to_f16(a0, &r0, &r1, bias);
+  i8x4_to_f16(a1, &r2, &r3, bias);
   v8h o;
   o[0] = r0[0]; o[1] = r0[1]; o[2] = r1[0]; o[3] = r1[1];
   o[4] = r2[0]; o[5] = r2[1]; o[6] = r3[0]; o[7] = r3[1];

@@ -6,20 +6,20 @@
 // gfx936 DCU" §3.3: paged INT8 K/V read directly, INT8 query and query scale, scales
 // restored after the integer accumulation, partitions merged; §1.3 score formula.)
 //
-// Stage 1 workgroup = (partition j, KV head g, sequence s), 8 waves. Wave w owns the
-// 64 tokens [64w, 64w+64) of the partition (4 pages). Per wave:
+// Stage 1 workgroup = (partition j, KV head g, sequence s), 8 waves. Wave w owns the 64
+// tokens [64w, 64w+64) of the partition (4 pages) and walks them page by page with an
+// online softmax, issuing loads two pages ahead of the page it computes. Per page:
 //  * QK on the int8 matrix cores as S^T = K . Q^T (v_mfma_i32_16x16x64_i8): the 16
-//    accumulator rows are 16 tokens of one page, the 16 columns are the 6 query heads
-//    of the group, repeated once (columns 6..11), then 4 zero columns. Each K operand
-//    load is one contiguous 1 KB per wave thanks to the K page layout.
-//  * scores s = qk * sQ * sK * sm_scale * log2(e) (exp2 domain), fp32 softmax over the
-//    64 tokens with column max/sum over the 4 lanes of a column.
-//  * PV in fp32-equivalent precision: w = p * (sV / max(sV)) lies in [0, 1]; columns 0..5
-//    carry fp16(w) and columns 6..11 carry fp16(w - fp16(w)), so hi + lo keeps 22
-//    significant bits; V codes are exact in fp16. v_mfma_f32_16x16x32_f16 computes
-//    out^T = V^T . P^T with fp32 accumulation; the two halves are summed with a DPP
-//    row shift. The wave's softmax state goes to LDS and the 8 states of the partition
-//    are merged into one partial (m, l, o[256]) per query head.
+//    accumulator rows are the 16 tokens of the page, the 16 columns are the 6 query
+//    heads of the group, repeated once (columns 6..11), then 4 zero columns. Each K
+//    operand load is one contiguous 1 KB per wave thanks to the K page layout.
+//  * scores s = qk * sQ * sK * sm_scale * log2(e) (exp2 domain), column max/sum over
+//    the 4 lanes that share a column.
+//  * PV in fp32-equivalent precision: w = p * (sV / max(sV)); columns 0..5 carry fp16(w)
+//    and columns 6..11 carry fp16(w - fp16(w)) (22 significant bits in all); V codes
+//    are exact in fp16. v_mfma_f32_16x16x16_f16 computes out^T = V^T . P^T with fp32
+//    accumulation; the halves are summed with a DPP row shift.
+// The 8 wave states are merged into one partial (m, l, o[256]) per query head.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -27,6 +27,14 @@ namespace i8a {
 
 constexpr int kPart = 512;
 constexpr int kDecWaves = 8;
+constexpr float kLazyRescale = 8.0f;  // log2 units
+
+// Workgroup barrier that orders LDS only: global loads issued before it stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __device__ __forceinline__ float from_lane_plus6(float v) {
   // DPP row_shl:6 -- lane i of each 16-lane row reads lane i + 6 of the same row.
@@ -46,181 +54,232 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
     int n_kv_heads, float qk_scale_log2, float* __restrict__ ws_m, float* __restrict__ ws_l,
     float* __restrict__ ws_o, int max_parts) {
   const int j = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The context length and this wave's 4 page ids are fetched together (one round
+  // trip); the table index is clamped so the fetch is safe before ctx is known.
+  const int32_t* trow = block_table + (size_t)s * max_blocks;
+  const int blk0 = j * (kPart / kPage) + 4 * w;
+  int pr[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) pr[t] = trow[min(blk0 + t, max_blocks - 1)];
   int ctx = ctx_lens[s];
+  // Consume all five scalar loads here so that none of them is sunk past the branch
+  // below (which would cost a second memory round trip before the K/V loads).
+  asm volatile("" ::"s"(ctx), "s"(pr[0]), "s"(pr[1]), "s"(pr[2]), "s"(pr[3]));
   ctx = ctx < 0 ? 0 : (ctx > ctx_cap ? ctx_cap : ctx);
   const int tok0 = j * kPart;
   if (tok0 >= ctx) return;  // whole workgroup: this partition is past the context
   const int n_tok = min(kPart, ctx - tok0);
 
-  __shared__ int s_pages[kPart / kPage];
   __shared__ __align__(16) int8_t s_q[kGroup][kHeadDim];
   __shared__ float s_qs[kGroup];
   __shared__ __align__(16) float s_ks[kPart];
   __shared__ __align__(16) float s_vs[kPart];
-  __shared__ float s_m[kDecWaves][kGroup], s_l[kDecWaves][kGroup];
+  __shared__ float s_m[kDecWaves][kGroup], s_l[kDecWaves][kGroup], s_f[kDecWaves];
   __shared__ __align__(16) float s_o[kDecWaves][kGroup][kHeadDim];
+  __shared__ __align__(16) float4 s_junk[64];  // sink for the stores of unused columns
+  __shared__ uint32_t s_bias;  // 0x80808080, read back after the barrier (see i8x4_to_f16)
 
-  // Block table of the partition -> LDS; query rows of the group -> int8 in LDS.
-  if (tid < kPart / kPage) {
-    const int blk = (tok0 >> 4) + tid;
-    int p = 0;
-    if (blk * kPage < ctx) {
-      p = block_table[(size_t)s * max_blocks + blk];
-      if (p < 0 || p >= num_pages) p = 0;
-    }
-    s_pages[tid] = p;
-  }
+  // Wave w owns tokens [64w, 64w+64) of the partition: pages 4w..4w+3 (wave-uniform page
+  // ids in scalar registers). Loads are issued in the order they are consumed (vmcnt
+  // order): query row and token scales, pages 0 and 1; the barrier then only waits for
+  // the query and the scales; pages 2 and 3 are issued two steps ahead of the page
+  // being computed, so each wave keeps about two pages (16 KB) in flight.
+  // A page past the context reads page 0 and its tokens are masked; waves 6 and 7
+  // re-read query row 5.
+  const int wtok0 = w * 64;
+  const int nvalid = min(64, n_tok - wtok0);  // <= 0: the wave has no tokens
+  int pg[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    pg[t] = (16 * t < nvalid && pr[t] >= 0 && pr[t] < num_pages) ? pr[t] : 0;
+  const size_t qrow = (size_t)s * n_q_heads + g * kGroup + min(w, kGroup - 1);
+  const uint2 qw = *reinterpret_cast<const uint2*>(q + qrow * kHeadDim + lane * 4);
+  const int pl = (lane >> 4) == 0 ? pg[0] : (lane >> 4) == 1 ? pg[1] : (lane >> 4) == 2 ? pg[2] : pg[3];
+  const size_t si = ((size_t)pl * n_kv_heads + g) * kPage + (lane & 15);
+  const float sk_l = k_scale[si];
+  const float sv_l = v_scale[si];
+  uint4 kA[4][4], vA[4][4];
+  auto issue_page = [&](int t) {
+    const size_t base = ((size_t)pg[t] * n_kv_heads + g) * kBlockBytes + lane * 16;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kA[t][u] = *reinterpret_cast<const uint4*>(k_cache + base + u * 1024);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) vA[t][u] = *reinterpret_cast<const uint4*>(v_cache + base + u * 1024);
+  };
+  __builtin_amdgcn_sched_barrier(0);
+  issue_page(0);
+  issue_page(1);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Quantize the group's query rows (waves 0..5) and stage them with the scales in LDS.
   if (w < kGroup) {
-    const size_t row = (size_t)s * n_q_heads + g * kGroup + w;
-    const uint2 qw = *reinterpret_cast<const uint2*>(q + row * kHeadDim + lane * 4);
     float sc;
     const uint32_t c = quantize4(bf16_to_f32(qw.x & 0xffffu), bf16_to_f32(qw.x >> 16),
                                  bf16_to_f32(qw.y & 0xffffu), bf16_to_f32(qw.y >> 16), &sc);
     *reinterpret_cast<uint32_t*>(&s_q[w][lane * 4]) = c;
     if (lane == 0) s_qs[w] = sc;
   }
-  __syncthreads();
-
-  // Issue this wave's K and V loads (4 pages x 4 KB each), then the token scales.
-  const int wtok0 = w * 64;
-  const int nvalid = min(64, n_tok - wtok0);  // <= 0: wave has no tokens
-  uint4 kA[4][4], vA[4][4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (wtok0 + 16 * t < n_tok) {
-      const size_t base = ((size_t)s_pages[4 * w + t] * n_kv_heads + g) * kBlockBytes + lane * 16;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) kA[t][u] = *reinterpret_cast<const uint4*>(k_cache + base + u * 1024);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) vA[t][u] = *reinterpret_cast<const uint4*>(v_cache + base + u * 1024);
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) { kA[t][u] = make_uint4(0, 0, 0, 0); vA[t][u] = make_uint4(0, 0, 0, 0); }
-    }
-  }
-  {
-    float a = 0.f, b = 0.f;
-    if (tid < n_tok) {
-      const size_t si = ((size_t)s_pages[tid >> 4] * n_kv_heads + g) * kPage + (tid & 15);
-      a = k_scale[si];
-      b = v_scale[si];
-    }
-    s_ks[tid] = a;
-    s_vs[tid] = b;
-  }
-  __syncthreads();
+  s_ks[wtok0 + lane] = sk_l;
+  s_vs[wtok0 + lane] = sv_l;
+  if (tid == 0) s_bias = 0x80808080u;
+  lds_barrier();
+  const uint32_t bias = s_bias;
 
   const int n = lane & 15, gq = lane >> 4;
   if (nvalid > 0) {
-    const int col_head = n < 2 * kGroup ? (n < kGroup ? n : n - kGroup) : -1;
+    const int col_head = n < 2 * kGroup ? (n < kGroup ? n : n - kGroup) : 0;
+    const float col_on = n < 2 * kGroup ? 1.f : 0.f;   // columns 12..15 carry nothing
     v4i qB[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      qB[u] = col_head >= 0 ? *reinterpret_cast<const v4i*>(&s_q[col_head][u * 64 + gq * 16])
-                            : v4i{0, 0, 0, 0};
-    v4i S[4];
+    for (int u = 0; u < 4; ++u) qB[u] = *reinterpret_cast<const v4i*>(&s_q[col_head][u * 64 + gq * 16]);
+    const float rs = s_qs[col_head] * qk_scale_log2;
+    // Scales of this lane's 16 tokens (16t + 4gq + i); masked tokens get sV = 0.
+    float kk[16], rv[16];
+    float svm = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      S[t] = v4i{0, 0, 0, 0};
+      const float4 a = *reinterpret_cast<const float4*>(&s_ks[wtok0 + 16 * t + 4 * gq]);
+      const float4 b = *reinterpret_cast<const float4*>(&s_vs[wtok0 + 16 * t + 4 * gq]);
+      kk[4 * t] = a.x; kk[4 * t + 1] = a.y; kk[4 * t + 2] = a.z; kk[4 * t + 3] = a.w;
+      rv[4 * t] = b.x; rv[4 * t + 1] = b.y; rv[4 * t + 2] = b.z; rv[4 * t + 3] = b.w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (16 * t + 4 * gq + i >= nvalid) rv[4 * t + i] = 0.f;
+        svm = fmaxf(svm, rv[4 * t + i]);
+      }
+    }
+    svm = col_max(svm);  // max V scale over the wave's 64 tokens (same in every lane)
+    const float inv = svm > 0.f ? 1.0f / svm : 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)  // the largest-scale token gets exactly 1
+      rv[e] = (rv[e] == svm ? 1.0f : rv[e] * inv) * col_on;
+
+    // Online softmax over the 4 pages. The reference max m_run only moves when a page
+    // max exceeds it by more than 2^8 (lazy rescale), so p <= 256 and w <= 256.
+    float m_run = -INFINITY, l_run = 0.f;
+    v4f O[16];
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) O[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t + 2 < 4) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_page(t + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      v4i S = v4i{0, 0, 0, 0};
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        S[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, kA[t][u]), qB[u], S[t],
-                                                     0, 0, 0);
-    }
-    const float rs = col_head >= 0 ? s_qs[col_head] * qk_scale_log2 : 0.f;
-    float x[16], sv[16];
-    float mx = -INFINITY, svm = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float4 kk = *reinterpret_cast<const float4*>(&s_ks[wtok0 + 16 * t + 4 * gq]);
-      const float4 vv = *reinterpret_cast<const float4*>(&s_vs[wtok0 + 16 * t + 4 * gq]);
-      const float kv4[4] = {kk.x, kk.y, kk.z, kk.w}, vv4[4] = {vv.x, vv.y, vv.z, vv.w};
+        S = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, kA[t][u]), qB[u], S, 0, 0, 0);
+      float x[4];
+      float bm = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool ok = 16 * t + 4 * gq + i < nvalid;
-        const float xv = ok ? (float)S[t][i] * kv4[i] * rs : -INFINITY;
-        x[4 * t + i] = xv;
-        sv[4 * t + i] = ok ? vv4[i] : 0.f;
-        mx = fmaxf(mx, xv);
-        svm = fmaxf(svm, sv[4 * t + i]);
+        x[i] = ok ? (float)S[i] * kk[4 * t + i] * rs : -INFINITY;
+        bm = fmaxf(bm, x[i]);
+      }
+      bm = col_max(bm);
+      if (__any(bm > m_run + kLazyRescale)) {
+        const float m_new = fmaxf(m_run, bm);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) O[dt] *= alpha;
+        m_run = m_new;
+      }
+      v4h B;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(x[i] - m_run);
+        l_run += p;
+        const float wv = p * rv[4 * t + i];
+        // columns 0..5: fp16(w); columns 6..11: fp16(w - fp16(w))
+        const float base = n >= kGroup ? (float)(_Float16)wv : 0.f;
+        B[i] = (_Float16)(wv - base);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) {
+        h2 lo, hi;
+        i8x4_to_f16(comp(vA[t][dt >> 2], dt & 3), &lo, &hi, bias);
+        const v4h A = {lo[0], lo[1], hi[0], hi[1]};
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, B, O[dt], 0, 0, 0);
       }
     }
-    mx = col_max(mx);
-    svm = col_max(svm);
-    float lsum = 0.f;
-    v8h B0, B1;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float p = exp2f(x[e] - mx);
-      lsum += p;
-      // sv / svm is a true division so that the largest-scale token gets exactly 1
-      // (a one-token context then returns fl32(code * scale) exactly).
-      const float wv = svm > 0.f ? p * (sv[e] / svm) : 0.f;
-      const _Float16 hi = (_Float16)wv;
-      const _Float16 val = n < kGroup ? hi : (n < 2 * kGroup ? (_Float16)(wv - (float)hi) : (_Float16)0.f);
-      if (e < 8) B0[e] = val; else B1[e - 8] = val;
-    }
-    lsum = col_sum(lsum);
-
+    l_run = col_sum(l_run);
+    // hi + lo columns; lanes of the unused columns store into s_junk.
+    float4* dst = n < kGroup ? reinterpret_cast<float4*>(&s_o[w][n][4 * gq]) : &s_junk[lane];
+    const int stride = n < kGroup ? 4 : 0;  // float4 units between dim tiles
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) {
-      const int q4 = dt >> 2, u = dt & 3;
-      const v8h A0 = i8x8_to_f16(comp(vA[0][q4], u), comp(vA[1][q4], u));
-      const v8h A1 = i8x8_to_f16(comp(vA[2][q4], u), comp(vA[3][q4], u));
-      v4f O = {0.f, 0.f, 0.f, 0.f};
-      O = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, B0, O, 0, 0, 0);
-      O = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, B1, O, 0, 0, 0);
       float4 r;
-      r.x = (O[0] + from_lane_plus6(O[0])) * svm;
-      r.y = (O[1] + from_lane_plus6(O[1])) * svm;
-      r.z = (O[2] + from_lane_plus6(O[2])) * svm;
-      r.w = (O[3] + from_lane_plus6(O[3])) * svm;
-      if (n < kGroup) *reinterpret_cast<float4*>(&s_o[w][n][16 * dt + 4 * gq]) = r;
+      r.x = O[dt][0] + from_lane_plus6(O[dt][0]);
+      r.y = O[dt][1] + from_lane_plus6(O[dt][1]);
+      r.z = O[dt][2] + from_lane_plus6(O[dt][2]);
+      r.w = O[dt][3] + from_lane_plus6(O[dt][3]);
+      dst[dt * stride] = r;
     }
     if (gq == 0 && n < kGroup) {
-      s_m[w][n] = mx;
-      s_l[w][n] = lsum;
+      s_m[w][n] = m_run;
+      s_l[w][n] = l_run;
     }
-  } else if (lane < kGroup) {
-    s_m[w][lane] = -INFINITY;
-    s_l[w][lane] = 0.f;
+    if (lane == 0) s_f[w] = svm;
+  } else {
+    // No tokens: an empty state (its weight in the merge below is exp2(-inf) = 0).
+    float4* o = reinterpret_cast<float4*>(&s_o[w][0][0]);
+#pragma unroll
+    for (int i = 0; i < kGroup * kHeadDim / 4 / 64; ++i) o[i * 64 + lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane < kGroup) {
+      s_m[w][lane] = -INFINITY;
+      s_l[w][lane] = 0.f;
+    }
+    if (lane == 0) s_f[w] = 0.f;
   }
-  __syncthreads();
+  lds_barrier();
 
-  // Merge the 8 wave states of this partition and write its partial.
-  for (int idx = tid; idx < kGroup * kHeadDim; idx += kDecWaves * 64) {
-    const int h = idx >> 8, d = idx & 255;
+  // Merge the 8 wave states of this partition: wave h < 6 merges query head h, lane l
+  // dims 4l..4l+3. A wave's stored output is in units of its max V scale (s_f).
+  if (w < kGroup) {
+    const int h = w;
+    float mw[kDecWaves];
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kDecWaves; ++ww) M = fmaxf(M, s_m[ww][h]);
-    float L = 0.f, O = 0.f;
+    for (int ww = 0; ww < kDecWaves; ++ww) {
+      mw[ww] = s_m[ww][h];
+      M = fmaxf(M, mw[ww]);
+    }
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int ww = 0; ww < kDecWaves; ++ww) {
-      const float mw = s_m[ww][h];
-      if (mw != -INFINITY) {
-        const float a = exp2f(mw - M);
-        L += a * s_l[ww][h];
-        O += a * s_o[ww][h][d];
-      }
+      const float a = __builtin_amdgcn_exp2f(mw[ww] - M);
+      L += a * s_l[ww][h];
+      const float af = a * s_f[ww];
+      const float4 ov = *reinterpret_cast<const float4*>(&s_o[ww][h][4 * lane]);
+      acc.x += af * ov.x; acc.y += af * ov.y; acc.z += af * ov.z; acc.w += af * ov.w;
     }
     const size_t pi = ((size_t)s * n_q_heads + g * kGroup + h) * max_parts + j;
-    ws_o[pi * kHeadDim + d] = O;
-    if (d == 0) {
+    *reinterpret_cast<float4*>(&ws_o[pi * kHeadDim + 4 * lane]) = acc;
+    if (lane == 0) {
       ws_m[pi] = M;
       ws_l[pi] = L;
     }
   }
 }
 
-// Stage 2: one workgroup per (q head, sequence), one thread per output dim.
+// Stage 2: one wave per (64-dim chunk, q head, sequence), online log-sum-exp over the
+// partitions in chunks of 64: lane j holds m_j and l_j, every lane loads o_j[d] of all
+// 64 partitions of the chunk up front (one memory round trip per chunk).
 // out = sum_j o_j 2^(m_j - M) / sum_j l_j 2^(m_j - M), M = max_j m_j.
-__global__ __launch_bounds__(256) void decode_merge_kernel(
+__global__ __launch_bounds__(64) void decode_merge_kernel(
     const float* __restrict__ ws_m, const float* __restrict__ ws_l, const float* __restrict__ ws_o,
     const int32_t* __restrict__ ctx_lens, int ctx_cap, int n_q_heads, int max_parts,
     float* __restrict__ out) {
-  const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
-  const int lane = d & 63, wv = d >> 6;
+  const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int d = c * 64 + lane;
   int ctx = ctx_lens[s];
   ctx = ctx < 0 ? 0 : (ctx > ctx_cap ? ctx_cap : ctx);
   const int P = (ctx + kPart - 1) / kPart;
@@ -230,42 +289,33 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     return;
   }
   const size_t base = ((size_t)s * n_q_heads + h) * max_parts;
-  __shared__ float s_red[4];
-  __shared__ float s_a[256], s_al[256];
-  float m = -INFINITY;
-  for (int jj = d; jj < P; jj += 256) m = fmaxf(m, ws_m[base + jj]);
-  m = wave_max(m);
-  if (lane == 0) s_red[wv] = m;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  float L = 0.f, O0 = 0.f, O1 = 0.f, O2 = 0.f, O3 = 0.f;
-  for (int c0 = 0; c0 < P; c0 += 256) {
-    const int jj = c0 + d;
-    float a = 0.f, al = 0.f;
-    if (jj < P) {
-      a = exp2f(ws_m[base + jj] - M);
-      al = a * ws_l[base + jj];
-    }
-    s_a[d] = a;
-    s_al[d] = al;
-    __syncthreads();
-    const int cnt = min(256, P - c0);
-    const float* op = ws_o + (base + c0) * kHeadDim + d;
-    int k = 0;
-    for (; k + 4 <= cnt; k += 4) {
-      O0 += s_a[k] * op[(size_t)k * kHeadDim];
-      O1 += s_a[k + 1] * op[(size_t)(k + 1) * kHeadDim];
-      O2 += s_a[k + 2] * op[(size_t)(k + 2) * kHeadDim];
-      O3 += s_a[k + 3] * op[(size_t)(k + 3) * kHeadDim];
-      L += (s_al[k] + s_al[k + 1]) + (s_al[k + 2] + s_al[k + 3]);
-    }
-    for (; k < cnt; ++k) {
-      O0 += s_a[k] * op[(size_t)k * kHeadDim];
-      L += s_al[k];
-    }
-    __syncthreads();
+  const float* pm = ws_m + base;
+  const float* pl = ws_l + base;
+  const float* po = ws_o + base * kHeadDim + d;
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  for (int j0 = 0; j0 < P; j0 += 64) {
+    const int cnt = min(64, P - j0);
+    const int jl = j0 + min(lane, cnt - 1);
+    const float mj0 = pm[jl], lj0 = pl[jl];
+    float oj[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) oj[i] = po[(size_t)(j0 + min(i, cnt - 1)) * kHeadDim];
+    const float mj = lane < cnt ? mj0 : -INFINITY;
+    const float cm = fmaxf(M, wave_max(mj));
+    const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - cm);
+    const float a = lane < cnt ? __builtin_amdgcn_exp2f(mj - cm) : 0.f;
+    float al = a * lj0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) al += __shfl_xor(al, off);
+    L = L * r + al;
+    float sacc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+      sacc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), i)) * oj[i];
+    acc = acc * r + sacc;
+    M = cm;
   }
-  o[d] = ((O0 + O1) + (O2 + O3)) / L;
+  o[d] = acc / L;
 }
 
 int launch_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cache,
@@ -285,8 +335,8 @@ int launch_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cach
                      ws_l, ws_o, max_parts);
   int rc = check_launch("attn_decode stage 1");
   if (rc) return rc;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(n_q_heads, num_seqs), dim3(256), 0, stream, ws_m,
-                     ws_l, ws_o, ctx_lens, ctx_cap, n_q_heads, max_parts, out);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(kHeadDim / 64, n_q_heads, num_seqs), dim3(64), 0,
+                     stream, ws_m, ws_l, ws_o, ctx_lens, ctx_cap, n_q_heads, max_parts, out);
   return check_launch("attn_decode stage 2");
 }
 
