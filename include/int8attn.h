@@ -39,12 +39,10 @@
  *    k_cache byte  ((p*H + h)*16 + d/16)*256 + o*16 + d%16
  *        = [page][head][d/16][o][d%16]: 16 dims of one token are one 16-byte run
  *          [DCU §2.3 chooses the same K blocking, [blocks, 4, 16, block_size, 16]].
- *    v_cache byte  (p*H + h)*4096 + (d/64)*1024 + (o/4)*256 + (d%16)*16
- *                  + ((d/16)%4)*4 + o%4
- *        = [page][head][d/64][o/4][d%16][(d/16)%4][o%4]: V is token-contiguous in runs
- *          of 4 tokens per dim [DCU §2.3 keeps V token-contiguous for the PV product];
- *          one 16-byte run holds 4 tokens x 4 dims whose dims are 16 apart, which is
- *          exactly one lane's operand bytes of the PV matrix product.
+ *    v_cache byte  (p*H + h)*4096 + d*16 + o
+ *        = [page][head][d][o]: the 16 tokens of one dim are one 16-byte run, which is
+ *          exactly one lane's operand bytes of the PV matrix product [DCU §2.3 keeps V
+ *          token-contiguous per output dim, [blocks, 4, 256, block_size]].
  *    k_scale / v_scale float  (p*H + h)*16 + o      [DCU §2.3: FP32 scales apart from
  *          the codes]
  *

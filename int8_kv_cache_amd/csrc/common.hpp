@@ -18,6 +18,13 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
+// Workgroup barrier that orders LDS only: global loads issued before it stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
@@ -30,14 +37,31 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Reductions over the 4 lanes {n, n+16, n+32, n+48} that share one column of a
-// 16x16 matrix-core accumulator (the column index is lane % 16).
+// 16x16 matrix-core accumulator (the column index is lane % 16). gfx950's lane swaps
+// stay in the VALU: permlane16_swap exchanges 16-lane rows 1<->0 and 3<->2 between its
+// two operands, permlane32_swap the two 32-lane halves, so combining the pair of results
+// of each swap reduces over lane xor 16 and then lane xor 32.
+__device__ __forceinline__ void swap16(float v, float* a, float* b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  *a = __uint_as_float(r[0]);
+  *b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float v, float* a, float* b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  *a = __uint_as_float(r[0]);
+  *b = __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float col_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  float a, b;
+  swap16(v, &a, &b);
+  swap32(fmaxf(a, b), &a, &b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float col_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  float a, b;
+  swap16(v, &a, &b);
+  swap32(a + b, &a, &b);
+  return a + b;
 }
 
 // Row quantizer for one row of 256 values spread over a wave, 4 per lane (lane l holds

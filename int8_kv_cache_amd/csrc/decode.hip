@@ -29,21 +29,10 @@ constexpr int kPart = 512;
 constexpr int kDecWaves = 8;
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
-// Workgroup barrier that orders LDS only: global loads issued before it stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 __device__ __forceinline__ float from_lane_plus6(float v) {
   // DPP row_shl:6 -- lane i of each 16-lane row reads lane i + 6 of the same row.
   return __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x106, 0xF, 0xF, true));
-}
-
-__device__ __forceinline__ uint32_t comp(const uint4& a, int u) {
-  return u == 0 ? a.x : (u == 1 ? a.y : (u == 2 ? a.z : a.w));
 }
 
 __global__ __launch_bounds__(512, 1) void decode_split_kernel(
@@ -100,13 +89,19 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
   const size_t si = ((size_t)pl * n_kv_heads + g) * kPage + (lane & 15);
   const float sk_l = k_scale[si];
   const float sv_l = v_scale[si];
-  uint4 kA[4][4], vA[4][4];
+  // K: four 1 KB wave loads per page. V: the A operand of dim tile dt is the dword of
+  // tokens 4gq..4gq+3 of dim 16dt + n, so each wave load covers 256 contiguous bytes.
+  uint4 kA[4][4];
+  uint32_t vA[4][16];
+  const int voff = (lane & 15) * 16 + (lane >> 4) * 4;
   auto issue_page = [&](int t) {
-    const size_t base = ((size_t)pg[t] * n_kv_heads + g) * kBlockBytes + lane * 16;
+    const size_t blk = ((size_t)pg[t] * n_kv_heads + g) * kBlockBytes;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) kA[t][u] = *reinterpret_cast<const uint4*>(k_cache + base + u * 1024);
+    for (int u = 0; u < 4; ++u)
+      kA[t][u] = *reinterpret_cast<const uint4*>(k_cache + blk + lane * 16 + u * 1024);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) vA[t][u] = *reinterpret_cast<const uint4*>(v_cache + base + u * 1024);
+    for (int dt = 0; dt < 16; ++dt)
+      vA[t][dt] = *reinterpret_cast<const uint32_t*>(v_cache + blk + voff + dt * 256);
   };
   __builtin_amdgcn_sched_barrier(0);
   issue_page(0);
@@ -203,7 +198,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) {
         h2 lo, hi;
-        i8x4_to_f16(comp(vA[t][dt >> 2], dt & 3), &lo, &hi, bias);
+        i8x4_to_f16(vA[t][dt], &lo, &hi, bias);
         const v4h A = {lo[0], lo[1], hi[0], hi[1]};
         O[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, B, O[dt], 0, 0, 0);
       }

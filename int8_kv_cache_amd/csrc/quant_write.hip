@@ -47,10 +47,10 @@ __global__ __launch_bounds__(256) void kv_quant_write_kernel(
   const size_t blk = ((size_t)page * n_kv_heads + head) * kBlockBytes;
   // K: dims 4l..4l+3 sit in chunk l/4 at byte (l%4)*4 of token o's 16-byte run.
   *reinterpret_cast<uint32_t*>(k_cache + blk + (lane >> 2) * 256 + o * 16 + (lane & 3) * 4) = kq;
-  // V: dim d = 4l + j -> (d/64) = l/16, (d%16) = 4(l%4)+j, (d/16)%4 = (l/4)%4.
-  int8_t* vb = v_cache + blk + (lane >> 4) * 1024 + (o >> 2) * 256 + ((lane >> 2) & 3) * 4 + (o & 3);
+  // V: dim d = 4l + j sits at byte d*16 + o (dim-major, the 16 tokens of a dim adjacent).
+  int8_t* vb = v_cache + blk + lane * 64 + o;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) vb[(4 * (lane & 3) + j) * 16] = (int8_t)(vq >> (8 * j));
+  for (int j = 0; j < 4; ++j) vb[j * 16] = (int8_t)(vq >> (8 * j));
   if (lane == 0) {
     const size_t si = ((size_t)page * n_kv_heads + head) * kPage + o;
     k_scale[si] = ks;

@@ -10,9 +10,9 @@ with H kv heads; every (p, h) owns one contiguous 4096-byte block in each array:
 
   K codes:  ((p*H + h) * 16 + d // 16) * 256 + o * 16 + d % 16
             -> [page][head][dim chunk of 16][token][16 dims]
-  V codes:  (p*H + h) * 4096 + (d // 64) * 1024 + (o // 4) * 256
-            + (d % 16) * 16 + ((d // 16) % 4) * 4 + o % 4
-            -> [page][head][dim quarter][token quad][dim mod 16][dim tile mod 4][token mod 4]
+  V codes:  (p*H + h) * 4096 + d * 16 + o
+            -> [page][head][dim][token]: the 16 tokens of one dim are one 16-byte run
+            (the article's V cache [blocks, heads, head_dim, block_size], §2.3)
   K and V scales (fp32): (p*H + h) * 16 + o
 
 These formulas are the library's published layout (its C header states the same
@@ -34,8 +34,7 @@ def k_offset(p, h, o, d, n_kv_heads):
 
 def v_offset(p, h, o, d, n_kv_heads):
     p, h, o, d = (np.asarray(a, dtype=np.int64) for a in (p, h, o, d))
-    return ((p * n_kv_heads + h) * BLOCK_BYTES + (d // 64) * 1024 + (o // 4) * 256
-            + (d % 16) * 16 + ((d // 16) % 4) * 4 + o % 4)
+    return (p * n_kv_heads + h) * BLOCK_BYTES + d * PAGE + o
 
 
 def scale_index(p, h, o, n_kv_heads):
