@@ -52,6 +52,31 @@ def quant_write_bytes(n_tokens: int, n_kv_heads: int, D: int) -> int:
     return n_tokens * (2 * n_kv_heads * D * 4 + 4 + n_kv_heads * (2 * D + 8))
 
 
+def recorded_traffic(kind: str):
+    """HBM bytes per launch of the `kind` ("prefill" or "decode") kernels, as measured by
+    the FETCH_SIZE / WRITE_SIZE counter passes summarised under profiles/ (scaled by a
+    copy of known size). Returned only while the kernel sources hash as they did when the
+    counters were taken; otherwise None (the figure would describe another kernel)."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "hbm_traffic_prefill_decode.md")
+    src = {"prefill": ["prefill.hip", "common.hpp"], "decode": ["decode.hip", "common.hpp"]}[kind]
+    try:
+        fields = {}
+        for line in open(path):
+            if ":" in line and line.strip().startswith(kind + "_"):
+                key, val = line.strip().split(":", 1)
+                fields[key] = val.strip()
+        h = hashlib.sha256()
+        for f in src:
+            h.update(open(os.path.join(root, "int8_kv_cache_amd", "csrc", f), "rb").read())
+        if h.hexdigest()[:16] != fields.get(kind + "_source_sha"):
+            return None
+        return int(fields[kind + "_traffic_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(dec_case, dec_data, pf_case, pf_data, budget_s=20.0):
     """The oracle, unchanged, on the host: decode at ctx 32768 (whole calls) and a
     sample of prefill query rows of the same chunk; quantization excluded."""
@@ -106,6 +131,9 @@ def main():
     ap.add_argument("--decode-copies", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed steps, one device-to-device copy of this many MiB "
+                         "(reference dispatch for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build measures the single-GPU path "
@@ -228,12 +256,20 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "prefill_chunk_kernel",
                      "achieved": round(pf_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
                      "frac": round(pf_tops / INT8_PEAK_TOPS, 4),
-                     "per_launch": pf_ops, "traffic": None},
+                     "per_launch": pf_ops, "traffic": recorded_traffic("prefill")},
         "roofline_decode": {"bound": "hbm", "kernel": "attn_decode (split + merge)",
                             "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "per_launch": dec_b,
-                            "traffic": None},
+                            "traffic": recorded_traffic("decode")},
     }
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         cb = cpu_baseline(dec, dec_data, pf, pf_data, args.cpu_budget)
         res["cpu_baseline"] = cb["decode"]
