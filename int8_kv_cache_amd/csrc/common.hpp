@@ -29,11 +29,20 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// Max / sum over all 64 lanes of a wave, result in every lane.
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+
+// Lane permutations inside a 16-lane row (DPP): lane ^ 1, lane ^ 2, mirror of each
+// 8-lane half, mirror of the row. Applied in that order they bring every lane of a row
+// the row's reduction.
+__device__ __forceinline__ float dpp(float v, int ctrl_sel) {
+  const int x = __builtin_bit_cast(int, v);
+  int r;
+  switch (ctrl_sel) {
+    case 0: r = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true); break;   // [1,0,3,2]
+    case 1: r = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true); break;   // [2,3,0,1]
+    case 2: r = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, true); break;  // half mirror
+    default: r = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, true); break; // mirror
+  }
+  return __builtin_bit_cast(float, r);
 }
 
 // Reductions over the 4 lanes {n, n+16, n+32, n+48} that share one column of a
@@ -62,6 +71,18 @@ __device__ __forceinline__ float col_sum(float v) {
   swap16(v, &a, &b);
   swap32(a + b, &a, &b);
   return a + b;
+}
+
+// Whole-wave max / sum without LDS: DPP inside each 16-lane row, then the row swaps.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v = fmaxf(v, dpp(v, k));
+  return col_max(v);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v += dpp(v, k);
+  return col_sum(v);
 }
 
 // Row quantizer for one row of 256 values spread over a wave, 4 per lane (lane l holds

@@ -266,7 +266,9 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
 
 // Stage 2: one wave per (64-dim chunk, q head, sequence), online log-sum-exp over the
 // partitions in chunks of 64: lane j holds m_j and l_j, every lane loads o_j[d] of all
-// 64 partitions of the chunk up front (one memory round trip per chunk).
+// 64 partitions of the chunk up front. The first chunk is loaded together with the
+// context length (indices clamped to the workspace), so a call with at most 64
+// partitions costs one memory round trip.
 // out = sum_j o_j 2^(m_j - M) / sum_j l_j 2^(m_j - M), M = max_j m_j.
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     const float* __restrict__ ws_m, const float* __restrict__ ws_l, const float* __restrict__ ws_o,
@@ -275,7 +277,20 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x;
   const int d = c * 64 + lane;
+  const size_t base = ((size_t)s * n_q_heads + h) * max_parts;
+  const float* pm = ws_m + base;
+  const float* pl = ws_l + base;
+  const float* po = ws_o + base * kHeadDim + d;
+  float mj0, lj0, oj[64];
+  auto load_chunk = [&](int j0, int cnt) {
+    const int jl = j0 + min(lane, cnt - 1);
+    mj0 = pm[jl];
+    lj0 = pl[jl];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) oj[i] = po[(size_t)(j0 + min(i, cnt - 1)) * kHeadDim];
+  };
   int ctx = ctx_lens[s];
+  load_chunk(0, min(64, max_parts));
   ctx = ctx < 0 ? 0 : (ctx > ctx_cap ? ctx_cap : ctx);
   const int P = (ctx + kPart - 1) / kPart;
   float* o = out + ((size_t)s * n_q_heads + h) * kHeadDim;
@@ -283,30 +298,30 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     o[d] = 0.f;
     return;
   }
-  const size_t base = ((size_t)s * n_q_heads + h) * max_parts;
-  const float* pm = ws_m + base;
-  const float* pl = ws_l + base;
-  const float* po = ws_o + base * kHeadDim + d;
+  __shared__ __align__(16) float s_a[64];  // the chunk's partition weights, broadcast
   float M = -INFINITY, L = 0.f, acc = 0.f;
   for (int j0 = 0; j0 < P; j0 += 64) {
     const int cnt = min(64, P - j0);
-    const int jl = j0 + min(lane, cnt - 1);
-    const float mj0 = pm[jl], lj0 = pl[jl];
-    float oj[64];
-#pragma unroll
-    for (int i = 0; i < 64; ++i) oj[i] = po[(size_t)(j0 + min(i, cnt - 1)) * kHeadDim];
+    if (j0 > 0) {
+      __syncthreads();  // the previous chunk's weights have been read
+      load_chunk(j0, cnt);
+    }
     const float mj = lane < cnt ? mj0 : -INFINITY;
     const float cm = fmaxf(M, wave_max(mj));
     const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - cm);
     const float a = lane < cnt ? __builtin_amdgcn_exp2f(mj - cm) : 0.f;
-    float al = a * lj0;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) al += __shfl_xor(al, off);
-    L = L * r + al;
+    L = L * r + wave_sum(a * (lane < cnt ? lj0 : 0.f));
+    s_a[lane] = a;
+    __syncthreads();
     float sacc = 0.f;
 #pragma unroll
-    for (int i = 0; i < 64; ++i)
-      sacc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), i)) * oj[i];
+    for (int i = 0; i < 64; i += 4) {
+      const float4 w4 = *reinterpret_cast<const float4*>(&s_a[i]);
+      sacc = fmaf(w4.x, i + 0 < cnt ? oj[i + 0] : 0.f, sacc);
+      sacc = fmaf(w4.y, i + 1 < cnt ? oj[i + 1] : 0.f, sacc);
+      sacc = fmaf(w4.z, i + 2 < cnt ? oj[i + 2] : 0.f, sacc);
+      sacc = fmaf(w4.w, i + 3 < cnt ? oj[i + 3] : 0.f, sacc);
+    }
     acc = acc * r + sacc;
     M = cm;
   }

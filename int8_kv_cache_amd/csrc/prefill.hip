@@ -11,9 +11,9 @@
 //
 // Workgroup = (32 query tokens, KV head g): 12 waves = the 6 query heads of the group x
 // two 16-token column tiles, i.e. 192 query rows that share every K/V byte staged in
-// LDS. The K/V of each 64-key block (4 pages, 32 KB) is double buffered in LDS and
-// moved by direct global->LDS loads issued one block ahead; one LDS-only barrier per
-// block hands the buffers over.
+// LDS. The K/V of each 64-key block (4 pages, 32 KB) is double buffered in LDS (two
+// distinct LDS variables, loop unrolled by two) and moved by direct global->LDS loads
+// issued one block ahead; one LDS-only barrier per block hands the buffers over.
 // Per wave and key block:
 //  * S^T = K . Q^T on v_mfma_i32_16x16x64_i8, 4 tiles t of 16 keys x 16 query tokens.
 //    Row r of tile t is token 4t + r%4 of page r/4, so lane group gq (lanes 16gq..)
@@ -42,48 +42,178 @@ constexpr int kPfPage = kBlockBytes + 64;  // LDS stride of a staged page: the 4
 
 // Moves one 64-key block (4 pages of K and of V, 32 KB) of KV head g into an LDS buffer
 // with direct global->LDS loads (global_load_lds_dwordx4: lane i of a wave lands at
-// LDS base + 16 i), 1 KB per wave instruction: chunk c (0..2047) is K (c < 1024) or V,
-// page t = (c >> 8) & 3, bytes (c & 255) * 16 of that page's 4 KB block, stored at
-// t * kPfPage + (c & 255) * 16. The 128 token scales go through one register per thread
-// so that slots past the context can be zeroed on the way.
+// LDS base + 16 i), 1 KB per wave instruction. Wave w < 8 moves quarter w % 4 of every
+// page of K (w < 4) or V; page t lands at t * kPfPage. Waves 8 and 9 move the 64 K / V
+// token scales (global_load_lds_dword, lane = key). Nothing waits here: the loads land
+// while the previous block is computed and are waited for once, before the barrier.
+// Page ids are fetched into scalar registers one block before their loads.
 struct BlockLoader {
   const int8_t* k_cache;
   const int8_t* v_cache;
   const float* k_scale;
   const float* v_scale;
   const int32_t* block_table;
-  int n_table, num_pages, n_kv_heads, g, ctx, tid, w, lane;
+  int n_table, num_pages, n_kv_heads, g, w, lane;
 
-  __device__ __forceinline__ int page(int kb, int t) const {
-    const int pi = kb * 4 + t;
-    const int p = pi < n_table ? block_table[pi] : 0;
-    return (p < 0 || p >= num_pages) ? 0 : p;
-  }
-  __device__ __forceinline__ void issue(int kb, int8_t (*kv_lds)[4 * kPfPage], float& sc) const {
+  struct Pages { int p[4]; };
+
+  // Raw table entries of block kb (the index is clamped; validity is checked at use).
+  __device__ __forceinline__ Pages pages(int kb) const {
+    Pages r;
 #pragma unroll
-    for (int it = 0; it < kPfPerThread; ++it) {
-      const int c0 = 64 * w + kPfThreads * it;  // first chunk of this wave's instruction
-      if (c0 < kPfChunks) {
-        const int kv = c0 >> 10, t = (c0 >> 8) & 3, off = (c0 & 255) * 16 + lane * 16;
-        const int8_t* src = (kv ? v_cache : k_cache) +
-                            ((size_t)page(kb, t) * n_kv_heads + g) * kBlockBytes + off;
+    for (int t = 0; t < 4; ++t) r.p[t] = block_table[min(kb * 4 + t, n_table - 1)];
+    return r;
+  }
+  // Entries past the context or outside the pool read page 0 (their keys are masked).
+  __device__ __forceinline__ int valid(const Pages& pg, int kb, int t) const {
+    const int p = pg.p[t];
+    return (kb * 4 + t >= n_table || p < 0 || p >= num_pages) ? 0 : p;
+  }
+  __device__ __forceinline__ void issue(const Pages& pg, int kb, int8_t (*kv_lds)[4 * kPfPage],
+                                        float (*sc_lds)[64]) const {
+    if (w < 8) {
+      const int kv = w >> 2, quarter = w & 3;
+      const int8_t* cache = kv ? v_cache : k_cache;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const size_t off = ((size_t)valid(pg, kb, t) * n_kv_heads + g) * kBlockBytes + quarter * 1024;
         __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)src,
-            (__attribute__((address_space(3))) void*)&kv_lds[kv][t * kPfPage + (c0 & 255) * 16],
+            (const __attribute__((address_space(1))) void*)(cache + off + lane * 16),
+            (__attribute__((address_space(3))) void*)&kv_lds[kv][t * kPfPage + quarter * 1024],
             16, 0, 0);
       }
+    } else if (w < 10) {  // K scales (wave 8) or V scales (wave 9); lane = key 16t + o
+      const int t = lane >> 4;
+      const int p0 = valid(pg, kb, 0), p1 = valid(pg, kb, 1), p2 = valid(pg, kb, 2),
+                p3 = valid(pg, kb, 3);
+      const int page = t == 0 ? p0 : t == 1 ? p1 : t == 2 ? p2 : p3;
+      const float* src = (w == 9 ? v_scale : k_scale) +
+                         ((size_t)page * n_kv_heads + g) * kPage + (lane & 15);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)&sc_lds[w - 8][0],
+                                       4, 0, 0);
     }
-    if (tid < 128) {
-      const int kv = tid >> 6, key = tid & 63;
-      const size_t si = ((size_t)page(kb, key >> 4) * n_kv_heads + g) * kPage + (key & 15);
-      sc = (kv ? v_scale : k_scale)[si];
-    }
-  }
-  // Call after the loads of `issue` have completed (vmcnt(0)).
-  __device__ __forceinline__ void put_scales(int kb, float (*sc_lds)[64], float sc) const {
-    if (tid < 128) sc_lds[tid >> 6][tid & 63] = kb * 64 + (tid & 63) < ctx ? sc : 0.f;
   }
 };
+
+// Per-lane constants of a wave's 16 query rows.
+struct RowCtx {
+  const int8_t* qcol;  // this lane's B-operand bytes of the query codes (LDS)
+  int koff, voff;      // A-operand byte offsets in a staged K / V block
+  int gq, lim, kfull, ctx;
+  float rs;            // sQ * sm_scale * log2(e), > 0
+};
+
+// Running softmax state of one lane: its query row's max and partial sum, and 64 of
+// the row's fp32 output accumulators (dims 16 dt + 4 gq + i).
+struct RowState {
+  float m_run, l_part;
+  v4f acc[16];
+};
+
+// One 64-key block: reads the staged block (sK/sV/sSk/sSv) and first issues the loads
+// of the next one into the other buffer (nKV/nSc). The two buffers are distinct LDS
+// variables, so the compiler can tell the in-flight direct-to-LDS writes from the reads
+// of this block and need not wait for them before reading.
+__device__ __forceinline__ void block_step(
+    int kb, int nkb, const BlockLoader& ld, BlockLoader::Pages& pg_next, const RowCtx& rc,
+    RowState& st, const int8_t* sK, const int8_t* sV, const float* sSk, const float* sSv,
+    int8_t (*nKV)[4 * kPfPage], float (*nSc)[64]) {
+  // QK: S[t] rows = tokens 4t..4t+3 of each of the 4 pages
+  v4i S[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) S[t] = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const v4i b = *reinterpret_cast<const v4i*>(rc.qcol + u * 64);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const v4i a = *reinterpret_cast<const v4i*>(sK + rc.koff + u * 1024 + t * 64);
+      S[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, S[t], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // bound the operand registers in flight
+  }
+  // The next block's loads go out once this block's query reads are issued.
+  if (kb + 1 < nkb) {
+    ld.issue(pg_next, kb + 1, nKV, nSc);
+    pg_next = ld.pages(kb + 2);
+  }
+  // y = qk * sK (key 16gq + 4t + i of the block), masked on diagonal / tail blocks only.
+  const int key0 = kb * 64;
+  const bool need_mask = (key0 + 64 > rc.kfull) || (key0 + 64 > rc.ctx);
+  float y[16], sv[16];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float4 sk = *reinterpret_cast<const float4*>(&sSk[16 * rc.gq + 4 * t]);
+    const float4 vs = *reinterpret_cast<const float4*>(&sSv[16 * rc.gq + 4 * t]);
+    y[4 * t] = (float)S[t][0] * sk.x;
+    y[4 * t + 1] = (float)S[t][1] * sk.y;
+    y[4 * t + 2] = (float)S[t][2] * sk.z;
+    y[4 * t + 3] = (float)S[t][3] * sk.w;
+    sv[4 * t] = vs.x; sv[4 * t + 1] = vs.y; sv[4 * t + 2] = vs.z; sv[4 * t + 3] = vs.w;
+  }
+  if (need_mask) {  // diagonal or context-tail block (wave-uniform)
+    // Masked keys (including slots past the context, whose scales are not data) get
+    // y = -inf and sV = 0, so their weight is exactly 0.
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (key0 + 16 * rc.gq + e >= rc.lim) {
+        y[e] = -INFINITY;
+        sv[e] = 0.f;
+      }
+  }
+  float ymax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) ymax = fmaxf(ymax, y[e]);
+  const float xmax = ymax * rc.rs;
+  if (__any(xmax > st.m_run + kLazyRescale)) {
+    const float m_new = fmaxf(st.m_run, col_max(xmax));
+    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) st.acc[dt] *= alpha;
+    st.l_part *= alpha;
+    st.m_run = m_new;
+  }
+  const float nm = -st.m_run;
+  float wm = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(y[e], rc.rs, nm));
+    st.l_part += p;
+    y[e] = p * sv[e];
+    wm = fmaxf(wm, y[e]);
+  }
+  wm = col_max(wm);
+  // 127 / wm via the hardware reciprocal (about 1 ulp): a code can move only at an
+  // exact rounding tie, and w * inv stays below 127.5, so codes never exceed 127.
+  const float inv = wm > 0.f ? 127.0f * __builtin_amdgcn_rcpf(wm) : 0.f;
+  const float sb = wm * (1.0f / 127.0f);
+  v4i Pb;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    uint32_t d = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * t + i] * inv, i, d);
+    Pb[t] = (int)d;
+  }
+
+  // PV: out^T(dim tile dt) += s_b * V^T(dt) . P^T; the A operand of lane (n, gq) is
+  // the 16 token codes of dim 16dt + n in page gq, one 16-byte LDS read.
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int dt = q4 * 4 + u;
+      const v4i a = *reinterpret_cast<const v4i*>(sV + rc.voff + dt * 256);
+      const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, Pb, v4i{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.acc[dt][i] = fmaf((float)r[i], sb, st.acc[dt][i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (kb + 1 < nkb) __builtin_amdgcn_s_waitcnt(0);  // the next block has landed in LDS
+  lds_barrier();
+}
 
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
     const uint16_t* __restrict__ q, int n_new, const int8_t* __restrict__ k_cache,
@@ -102,19 +232,21 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
   const int pos0 = ctx - n_new;
   const int kend = causal ? pos0 + t0 + nq : ctx;  // keys [0, kend) are needed
   const int nkb = (kend + 63) >> 6;
-  const int kfull = causal ? pos0 + t0 + 1 : ctx;  // keys < kfull are seen by every row
   const int my_tok = t0 + 16 * half + n;            // this lane's query token
-  const int lim = causal ? min(pos0 + my_tok + 1, ctx) : ctx;  // keys < lim are visible
 
-  __shared__ __align__(16) int8_t s_kv[2][2][4 * kPfPage];       // [buffer][K,V][4 pages]
-  __shared__ __align__(16) float s_sc[2][2][64];                 // [buffer][K,V][key]
+  // Two K/V buffers and two scale buffers, each its own LDS variable.
+  __shared__ __align__(16) int8_t s_kv0[2][4 * kPfPage];  // [K,V][4 pages]
+  __shared__ __align__(16) int8_t s_kv1[2][4 * kPfPage];
+  __shared__ __align__(16) float s_sc0[2][64];            // [K,V][key]
+  __shared__ __align__(16) float s_sc1[2][64];
   __shared__ __align__(16) int8_t s_q[kGroup * kPfTok][kQStride];  // query codes
   __shared__ float s_qs[kGroup][kPfTok];
 
   const BlockLoader ld{k_cache, v_cache, k_scale, v_scale, block_table, (ctx + kPage - 1) / kPage,
-                       num_pages, n_kv_heads, g, ctx, tid, w, lane};
-  float sc_next = 0.f;
-  if (nkb > 0) ld.issue(0, s_kv[0], sc_next);  // first block in flight during the Q work
+                       num_pages, n_kv_heads, g, w, lane};
+  BlockLoader::Pages pg_next = ld.pages(0);
+  if (nkb > 0) ld.issue(pg_next, 0, s_kv0, s_sc0);  // first block in flight during the Q work
+  pg_next = ld.pages(1);
 
   // ---- quantize this wave's 16 query rows (head h); rows past the chunk are zero.
   int8_t* qrows = &s_q[hl * kPfTok + 16 * half][0];
@@ -136,128 +268,44 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
-  if (nkb > 0) ld.put_scales(0, s_sc[0], sc_next);
   lds_barrier();
-  const int8_t* qcol = qrows + n * kQStride + gq * 16;  // this lane's B-operand bytes
+
+  RowCtx rc;
+  rc.qcol = qrows + n * kQStride + gq * 16;
   // A-operand bytes: QK row n = token 4t + n%4 of page n/4 (dims 64u + 16gq..),
   // PV row n of dim tile dt = dim 16dt + n of page gq (its 16 tokens).
-  const int koff = (n >> 2) * kPfPage + gq * 256 + (n & 3) * 16;
-  const int voff = gq * kPfPage + n * 16;
+  rc.koff = (n >> 2) * kPfPage + gq * 256 + (n & 3) * 16;
+  rc.voff = gq * kPfPage + n * 16;
+  rc.gq = gq;
+  rc.lim = causal ? min(pos0 + my_tok + 1, ctx) : ctx;  // keys < lim are visible
+  rc.kfull = causal ? pos0 + t0 + 1 : ctx;              // keys < kfull are seen by every row
+  rc.ctx = ctx;
   // rs > 0 keeps max(x) = rs * max(y) and exp2(fma(y, rs, -m)) = 0 for masked y = -inf.
-  const float rs = fmaxf(s_qs[hl][16 * half + n] * qk_scale_log2, 1e-30f);
+  rc.rs = fmaxf(s_qs[hl][16 * half + n] * qk_scale_log2, 1e-30f);
 
-  float m_run = -INFINITY, l_part = 0.f;
-  v4f acc[16];
+  RowState st;
+  st.m_run = -INFINITY;
+  st.l_part = 0.f;
 #pragma unroll
-  for (int dt = 0; dt < 16; ++dt) acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < 16; ++dt) st.acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) ld.issue(kb + 1, s_kv[buf ^ 1], sc_next);
-    const int8_t* sK = s_kv[buf][0];
-    const int8_t* sV = s_kv[buf][1];
-
-    // QK: S[t] rows = tokens 4t..4t+3 of each of the 4 pages
-    v4i S[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) S[t] = v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const v4i b = *reinterpret_cast<const v4i*>(qcol + u * 64);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const v4i a = *reinterpret_cast<const v4i*>(sK + koff + u * 1024 + t * 64);
-        S[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, S[t], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // bound the operand registers in flight
-    }
-    // y = qk * sK (key 16gq + 4t + i of the block), masked on diagonal / tail blocks only.
-    const int key0 = kb * 64;
-    const bool need_mask = (key0 + 64 > kfull) || (key0 + 64 > ctx);
-    float y[16];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float4 sk = *reinterpret_cast<const float4*>(&s_sc[buf][0][16 * gq + 4 * t]);
-      y[4 * t] = (float)S[t][0] * sk.x;
-      y[4 * t + 1] = (float)S[t][1] * sk.y;
-      y[4 * t + 2] = (float)S[t][2] * sk.z;
-      y[4 * t + 3] = (float)S[t][3] * sk.w;
-    }
-    if (need_mask) {  // diagonal or context-tail block (wave-uniform)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (key0 + 16 * gq + e >= lim) y[e] = -INFINITY;
-    }
-    float ymax = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) ymax = fmaxf(ymax, y[e]);
-    const float xmax = ymax * rs;
-    if (__any(xmax > m_run + kLazyRescale)) {
-      const float m_new = fmaxf(m_run, col_max(xmax));
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int dt = 0; dt < 16; ++dt) acc[dt] *= alpha;
-      l_part *= alpha;
-      m_run = m_new;
-    }
-    const float nm = -m_run;
-    float wm = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float4 sv = *reinterpret_cast<const float4*>(&s_sc[buf][1][16 * gq + 4 * t]);
-      const float svv[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(y[4 * t + i], rs, nm));
-        l_part += p;
-        const float wv = p * svv[i];
-        y[4 * t + i] = wv;
-        wm = fmaxf(wm, wv);
-      }
-    }
-    wm = col_max(wm);
-    const float inv = wm > 0.f ? 127.0f / wm : 0.f;
-    const float sb = wm * (1.0f / 127.0f);
-    v4i Pb;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      uint32_t d = 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * t + i] * inv, i, d);
-      Pb[t] = (int)d;
-    }
-
-    // PV: out^T(dim tile dt) += s_b * V^T(dt) . P^T; the A operand of lane (n, gq) is
-    // the 16 token codes of dim 16dt + n in page gq, one 16-byte LDS read.
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int dt = q4 * 4 + u;
-        const v4i a = *reinterpret_cast<const v4i*>(sV + voff + dt * 256);
-        const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, Pb, v4i{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[dt][i] = fmaf((float)r[i], sb, acc[dt][i]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (kb + 1 < nkb) {
-      __builtin_amdgcn_s_waitcnt(0);  // the next block has landed in LDS
-      ld.put_scales(kb + 1, s_sc[buf ^ 1], sc_next);
-    }
-    lds_barrier();
+  for (int kb = 0; kb < nkb; kb += 2) {
+    block_step(kb, nkb, ld, pg_next, rc, st, s_kv0[0], s_kv0[1], s_sc0[0], s_sc0[1], s_kv1, s_sc1);
+    if (kb + 1 < nkb)
+      block_step(kb + 1, nkb, ld, pg_next, rc, st, s_kv1[0], s_kv1[1], s_sc1[0], s_sc1[1], s_kv0,
+                 s_sc0);
   }
 
   // ---- normalise and store: lane (n, gq) holds dims 16*dt + 4*gq + i of its row.
-  const float l = col_sum(l_part);
+  const float l = col_sum(st.l_part);
   if (my_tok < t0 + nq) {
     const float il = 1.0f / l;
     float* o = out + ((size_t)my_tok * n_q_heads + h) * kHeadDim + 4 * gq;
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) {
       float4 v;
-      v.x = acc[dt][0] * il; v.y = acc[dt][1] * il;
-      v.z = acc[dt][2] * il; v.w = acc[dt][3] * il;
+      v.x = st.acc[dt][0] * il; v.y = st.acc[dt][1] * il;
+      v.z = st.acc[dt][2] * il; v.w = st.acc[dt][3] * il;
       *reinterpret_cast<float4*>(o + 16 * dt) = v;
     }
   }
