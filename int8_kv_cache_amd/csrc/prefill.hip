@@ -36,14 +36,16 @@ constexpr int kPfThreads = kPfWaves * 64;  // 768
 constexpr int kPfChunks = 2048;            // 16-byte chunks of one 64-key K+V block
 constexpr int kPfPerThread = (kPfChunks + kPfThreads - 1) / kPfThreads;  // 3
 constexpr float kLazyRescale = 8.0f;       // log2 units
-constexpr int kQStride = kHeadDim + 16;    // padded LDS row of query codes (no bank conflicts)
-constexpr int kPfPage = kBlockBytes + 64;  // LDS stride of a staged page: the 4 pages of a
-                                           // block start on different banks
+constexpr int kXcds = 8;                   // XCDs of an MI355X
+constexpr int kQStride = kHeadDim + 32;    // padded LDS row of query codes (no bank conflicts)
+constexpr int kPfPage = kBlockBytes + 64;  // LDS stride of a staged K page: the 4 pages of a
+                                           // block start on different banks (V pages are
+                                           // read one page per lane group and need none)
 
 // Moves one 64-key block (4 pages of K and of V, 32 KB) of KV head g into an LDS buffer
 // with direct global->LDS loads (global_load_lds_dwordx4: lane i of a wave lands at
 // LDS base + 16 i), 1 KB per wave instruction. Wave w < 8 moves quarter w % 4 of every
-// page of K (w < 4) or V; page t lands at t * kPfPage. Waves 8 and 9 move the 64 K / V
+// page of K (w < 4) or V; K page t lands at t * kPfPage, V page t at t * 4096. Waves 8 and 9 move the 64 K / V
 // token scales (global_load_lds_dword, lane = key). Nothing waits here: the loads land
 // while the previous block is computed and are waited for once, before the barrier.
 // Page ids are fetched into scalar registers one block before their loads.
@@ -79,7 +81,7 @@ struct BlockLoader {
         const size_t off = ((size_t)valid(pg, kb, t) * n_kv_heads + g) * kBlockBytes + quarter * 1024;
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)(cache + off + lane * 16),
-            (__attribute__((address_space(3))) void*)&kv_lds[kv][t * kPfPage + quarter * 1024],
+            (__attribute__((address_space(3))) void*)&kv_lds[kv][t * (kv ? kBlockBytes : kPfPage) + quarter * 1024],
             16, 0, 0);
       }
     } else if (w < 10) {  // K scales (wave 8) or V scales (wave 9); lane = key 16t + o
@@ -220,8 +222,22 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
     const int8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int ctx,
     int causal, int num_pages, int n_q_heads, int n_kv_heads, float qk_scale_log2,
-    float* __restrict__ out) {
-  const int qb = blockIdx.x, g = blockIdx.y;
+    float* __restrict__ out, int n_qb, int xcd_per_head) {
+  // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs (linear id
+  // mod 8), so give each KV head its own XCDs (8 / H of them when H divides 8). Each
+  // XCD's L2 then streams the K/V of one head instead of all of them.
+  int qb, g;
+  {
+    const int L = blockIdx.x, xcd = L % kXcds, slot = L / kXcds;
+    if (xcd_per_head > 0) {
+      g = xcd / xcd_per_head;
+      qb = slot * xcd_per_head + xcd % xcd_per_head;
+    } else {
+      g = L / n_qb;
+      qb = L % n_qb;
+    }
+    if (qb >= n_qb || g >= n_kv_heads) return;  // padding workgroup (whole block)
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = w >> 1, half = w & 1;  // head within the group, 16-token half
@@ -275,7 +291,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
   // A-operand bytes: QK row n = token 4t + n%4 of page n/4 (dims 64u + 16gq..),
   // PV row n of dim tile dt = dim 16dt + n of page gq (its 16 tokens).
   rc.koff = (n >> 2) * kPfPage + gq * 256 + (n & 3) * 16;
-  rc.voff = gq * kPfPage + n * 16;
+  rc.voff = gq * kBlockBytes + n * 16;
   rc.gq = gq;
   rc.lim = causal ? min(pos0 + my_tok + 1, ctx) : ctx;  // keys < lim are visible
   rc.kfull = causal ? pos0 + t0 + 1 : ctx;              // keys < kfull are seen by every row
@@ -315,10 +331,17 @@ int launch_prefill(const uint16_t* q, int n_new, const int8_t* k_cache, const in
                    const float* k_scale, const float* v_scale, const int32_t* block_table,
                    int ctx, int causal, int num_pages, int n_q_heads, int n_kv_heads,
                    float sm_scale, float* out, hipStream_t stream) {
-  const dim3 grid((n_new + kPfTok - 1) / kPfTok, n_kv_heads);
-  hipLaunchKernelGGL(prefill_chunk_kernel, grid, dim3(kPfThreads), 0, stream, q, n_new, k_cache,
-                     v_cache, k_scale, v_scale, block_table, ctx, causal, num_pages, n_q_heads,
-                     n_kv_heads, sm_scale * kLog2e, out);
+  const int n_qb = (n_new + kPfTok - 1) / kPfTok;
+  // Heads spread over the XCDs when the head count divides their number; otherwise the
+  // plain (head-major) order.
+  const int xcd_per_head = (n_kv_heads <= kXcds && kXcds % n_kv_heads == 0) ? kXcds / n_kv_heads : 0;
+  const long long n_wg = xcd_per_head > 0
+                             ? (long long)kXcds * ((n_qb + xcd_per_head - 1) / xcd_per_head)
+                             : (long long)n_qb * n_kv_heads;
+  hipLaunchKernelGGL(prefill_chunk_kernel, dim3((unsigned)n_wg), dim3(kPfThreads), 0, stream, q,
+                     n_new, k_cache, v_cache, k_scale, v_scale, block_table, ctx, causal,
+                     num_pages, n_q_heads, n_kv_heads, sm_scale * kLog2e, out, n_qb,
+                     xcd_per_head);
   return check_launch("attn_prefill_chunk");
 }
 
