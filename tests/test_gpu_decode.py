@@ -117,3 +117,13 @@ def test_config5_sampled():
     keep = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 5, 17, 60})
     st = DecodeSetup(case, keep=keep)
     _check_all(st, keep)
+
+
+@pytest.mark.parametrize("n_kv", [1, 3])
+def test_decode_other_kv_head_counts(n_kv):
+    need_gpu()
+    ctx = [1, 700, 1537]
+    say(f"attn_decode ctx {ctx} with {n_kv} KV heads x 6 query heads")
+    case = workloads.make_decode_case(80 + n_kv, ctx, pages="random", k_outliers=4,
+                                      n_q_heads=6 * n_kv, n_kv_heads=n_kv)
+    _check_all(DecodeSetup(case))

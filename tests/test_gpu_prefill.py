@@ -71,3 +71,15 @@ def test_prefill_rows_match_decode_at_matching_context():
     dec = dec.cpu().numpy()
     for i, t in enumerate(rows):
         assert np.max(np.abs(out[t] - dec[i])) <= TOL_A * st.vmax
+
+
+@pytest.mark.parametrize("n_kv", [1, 2, 3, 5])
+def test_prefill_other_kv_head_counts(n_kv):
+    # 1 and 2 KV heads take the per-XCD tile order (with padding workgroups when the chunk
+    # has fewer query blocks than XCDs per head); 3 and 5 take the plain order.
+    need_gpu()
+    say(f"attn_prefill_chunk ctx=400 n_new=90 with {n_kv} KV heads x 6 query heads")
+    case = workloads.make_prefill_case(70 + n_kv, 400, 90, k_outliers=4,
+                                       n_q_heads=6 * n_kv, n_kv_heads=n_kv)
+    st = PrefillSetup(case)
+    _check(st, np.arange(case.n_new))
