@@ -108,3 +108,23 @@ def test_q_quant_bit_exact():
     rc, rs = quant.quantize_rows(quant.bf16_bits_to_f32(ties))
     assert np.array_equal(codes.cpu().numpy(), rc)
     assert np.array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("in_bf16", [False, True])
+def test_page_runs_and_scattered_slots_in_one_call(in_bf16):
+    # Groups of 16 tokens: a whole page in order (written as whole blocks), the same page
+    # size in reverse order, a run that starts mid-page, a whole page then a skipped
+    # token inside the next run, and a ragged tail; all must equal the oracle's scatter.
+    need_gpu()
+    rng = np.random.default_rng(91)
+    runs = [np.arange(48, 64),                 # page 3, in order
+            np.arange(80, 96)[::-1],           # page 5, reversed
+            np.arange(104, 120),               # starts at offset 8 of page 6
+            np.arange(16, 32),                 # page 1, in order
+            np.r_[np.arange(128, 135), -1, np.arange(136, 144)],  # page 8 with a skipped token
+            np.array([200, 7, 250])]           # ragged tail, scattered
+    slots = np.concatenate(runs).astype(np.int32)
+    T, H = slots.shape[0], 2
+    k = rng.standard_normal((T, H, 256), dtype=np.float32) * np.float32(2.5)
+    v = rng.standard_normal((T, H, 256), dtype=np.float32)
+    _write_and_compare(k, v, slots, num_pages=17, H=H, in_bf16=in_bf16)
