@@ -89,19 +89,20 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
   const size_t si = ((size_t)pl * n_kv_heads + g) * kPage + (lane & 15);
   const float sk_l = k_scale[si];
   const float sv_l = v_scale[si];
-  // K: four 1 KB wave loads per page. V: the A operand of dim tile dt is the dword of
-  // tokens 4gq..4gq+3 of dim 16dt + n, so each wave load covers 256 contiguous bytes.
+  // K and V: four 1 KB wave loads per page each (lane l reads bytes 16l.. of each KB).
+  // V lane (n, gq) thus receives all 16 tokens of dim 16(4q + gq) + n for q = 0..3; a 4x4
+  // transpose over the lanes of its column (gfx950 lane swaps) gives it the A operand of
+  // every dim tile: tokens 4gq..4gq+3 of dim 16dt + n.
   uint4 kA[4][4];
-  uint32_t vA[4][16];
-  const int voff = (lane & 15) * 16 + (lane >> 4) * 4;
+  uint4 vL[4][4];
   auto issue_page = [&](int t) {
     const size_t blk = ((size_t)pg[t] * n_kv_heads + g) * kBlockBytes;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       kA[t][u] = *reinterpret_cast<const uint4*>(k_cache + blk + lane * 16 + u * 1024);
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt)
-      vA[t][dt] = *reinterpret_cast<const uint32_t*>(v_cache + blk + voff + dt * 256);
+    for (int u = 0; u < 4; ++u)
+      vL[t][u] = *reinterpret_cast<const uint4*>(v_cache + blk + lane * 16 + u * 1024);
   };
   __builtin_amdgcn_sched_barrier(0);
   issue_page(0);
@@ -195,10 +196,23 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
         const float base = n >= kGroup ? (float)(_Float16)wv : 0.f;
         B[i] = (_Float16)(wv - base);
       }
+      // Lane (n, gq) loaded dim 16(4q + gq) + n, all 16 tokens; transpose the 4x4 dwords
+      // over the lanes {n, n+16, n+32, n+48} so that it holds tokens 4gq..4gq+3 of dims
+      // 16(4q + c) + n, c = 0..3.
+      uint32_t vA[16];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        uint32_t r0 = vL[t][qq].x, r1 = vL[t][qq].y, r2 = vL[t][qq].z, r3 = vL[t][qq].w;
+        auto p = __builtin_amdgcn_permlane32_swap(r0, r2, false, false); r0 = p[0]; r2 = p[1];
+        p = __builtin_amdgcn_permlane32_swap(r1, r3, false, false); r1 = p[0]; r3 = p[1];
+        p = __builtin_amdgcn_permlane16_swap(r0, r1, false, false); r0 = p[0]; r1 = p[1];
+        p = __builtin_amdgcn_permlane16_swap(r2, r3, false, false); r2 = p[0]; r3 = p[1];
+        vA[4 * qq] = r0; vA[4 * qq + 1] = r1; vA[4 * qq + 2] = r2; vA[4 * qq + 3] = r3;
+      }
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) {
         h2 lo, hi;
-        i8x4_to_f16(vA[t][dt], &lo, &hi, bias);
+        i8x4_to_f16(vA[dt], &lo, &hi, bias);
         const v4h A = {lo[0], lo[1], hi[0], hi[1]};
         O[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, B, O[dt], 0, 0, 0);
       }
