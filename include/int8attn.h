@@ -172,6 +172,8 @@ int attn_decode(const uint16_t* q,
  *  scale = max_k(p_k * sV_k) / 127 and multiplied with the V codes on the int8 matrix
  *  cores; the softmax denominator sums the unquantized weights.
  *  out           fp32 [n_new][n_q_heads][head_dim], fully overwritten.
+ *  num_pages * n_kv_heads * 16 must stay below 2^32 (scale index range), else
+ *  I8A_EUNSUPPORTED.
  *  n_new == 0 is a no-op returning I8A_OK. */
 int attn_prefill_chunk(const uint16_t* q, int n_new,
                        const int8_t* k_cache, const int8_t* v_cache,

@@ -128,6 +128,9 @@ int attn_prefill_chunk(const uint16_t* q, int n_new, const int8_t* k_cache, cons
     return set_error(I8A_EINVAL, "attn_prefill_chunk: n_new %d, context_len %d, num_pages %d, causal %d",
                      n_new, context_len, num_pages, causal);
   if (context_len > 2147483000 - 64) return set_error(I8A_EINVAL, "attn_prefill_chunk: context too long");
+  if ((long long)num_pages * n_kv_heads * 16 >= (1ll << 32))
+    return set_error(I8A_EUNSUPPORTED, "attn_prefill_chunk: num_pages %d x %d heads exceeds the scale index range",
+                     num_pages, n_kv_heads);
   if (!isfinite(sm_scale)) return set_error(I8A_EINVAL, "attn_prefill_chunk: sm_scale not finite");
   if (n_new == 0) return I8A_OK;
   if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_table || !out)

@@ -25,6 +25,10 @@
 //  * w = p * sV, per (row, block) s_b = max w / 127, codes rint(w / s_b) in [0, 127]
 //    (v_cvt_pk_u8_f32 converts and packs); the denominator sums the unquantized p;
 //  * out^T += s_b * (V^T . P^T) on v_mfma_i32_16x16x64_i8, exact in int32 per block.
+//    The product is accumulated onto the bit pattern of 1.5 * 2^23 (|V^T . P^T| <=
+//    64 * 127 * 127 < 2^22), so read as fp32 it is 1.5 * 2^23 + the exact integer and
+//    one fma folds it in; the offsets s_b * 1.5 * 2^23 are summed per row and taken
+//    out every 8 blocks and at the end.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -36,6 +40,9 @@ constexpr int kPfThreads = kPfWaves * 64;  // 768
 constexpr int kPfChunks = 2048;            // 16-byte chunks of one 64-key K+V block
 constexpr int kPfPerThread = (kPfChunks + kPfThreads - 1) / kPfThreads;  // 3
 constexpr float kLazyRescale = 8.0f;       // log2 units
+constexpr float kMagicF = 12582912.0f;   // 1.5 * 2^23
+constexpr v4i kMagic4 = {0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};  // its bits
+constexpr int kFlushBlocks = 8;           // blocks between removals of the offsets
 constexpr int kXcds = 8;                   // XCDs of an MI355X
 constexpr int kQStride = kHeadDim + 32;    // padded LDS row of query codes (no bank conflicts)
 constexpr int kPfPage = kBlockBytes + 64;  // LDS stride of a staged K page: the 4 pages of a
@@ -79,8 +86,11 @@ struct BlockLoader {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const size_t off = ((size_t)valid(pg, kb, t) * n_kv_heads + g) * kBlockBytes + quarter * 1024;
+        const int8_t* wave_src = cache + off;  // uniform; the lane offset stays 32-bit
+        uint32_t lo = lane * 16;
+        asm volatile("" : "+v"(lo));  // keeps (scalar base, 32-bit lane offset) addressing
         __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(cache + off + lane * 16),
+            (const __attribute__((address_space(1))) void*)(wave_src + lo),
             (__attribute__((address_space(3))) void*)&kv_lds[kv][t * (kv ? kBlockBytes : kPfPage) + quarter * 1024],
             16, 0, 0);
       }
@@ -89,8 +99,10 @@ struct BlockLoader {
       const int p0 = valid(pg, kb, 0), p1 = valid(pg, kb, 1), p2 = valid(pg, kb, 2),
                 p3 = valid(pg, kb, 3);
       const int page = t == 0 ? p0 : t == 1 ? p1 : t == 2 ? p2 : p3;
-      const float* src = (w == 9 ? v_scale : k_scale) +
-                         ((size_t)page * n_kv_heads + g) * kPage + (lane & 15);
+      // 32-bit element index: the launcher checks num_pages * n_kv_heads * 16 < 2^32.
+      const uint32_t off = ((uint32_t)page * (uint32_t)n_kv_heads + (uint32_t)g) * kPage + (lane & 15);
+      const float* src = (w == 9 ? v_scale : k_scale) + off;
+      asm volatile("" : "+v"(src));  // computed here, not kept live across the loop
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)&sc_lds[w - 8][0],
                                        4, 0, 0);
@@ -106,10 +118,10 @@ struct RowCtx {
   float rs;            // sQ * sm_scale * log2(e), > 0
 };
 
-// Running softmax state of one lane: its query row's max and partial sum, and 64 of
-// the row's fp32 output accumulators (dims 16 dt + 4 gq + i).
+// Running softmax state of one lane: its query row's max and partial sum, 64 of the
+// row's fp32 output accumulators (dims 16 dt + 4 gq + i), and the offset they carry.
 struct RowState {
-  float m_run, l_part;
+  float m_run, l_part, corr;
   v4f acc[16];
 };
 
@@ -174,6 +186,7 @@ __device__ __forceinline__ void block_step(
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) st.acc[dt] *= alpha;
     st.l_part *= alpha;
+    st.corr *= alpha;
     st.m_run = m_new;
   }
   const float nm = -st.m_run;
@@ -207,11 +220,17 @@ __device__ __forceinline__ void block_step(
     for (int u = 0; u < 4; ++u) {
       const int dt = q4 * 4 + u;
       const v4i a = *reinterpret_cast<const v4i*>(sV + rc.voff + dt * 256);
-      const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, Pb, v4i{0, 0, 0, 0}, 0, 0, 0);
+      const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, Pb, kMagic4, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st.acc[dt][i] = fmaf((float)r[i], sb, st.acc[dt][i]);
+      for (int i = 0; i < 4; ++i) st.acc[dt][i] = fmaf(__int_as_float(r[i]), sb, st.acc[dt][i]);
     }
     __builtin_amdgcn_sched_barrier(0);
+  }
+  st.corr = fmaf(sb, kMagicF, st.corr);
+  if ((kb & (kFlushBlocks - 1)) == kFlushBlocks - 1) {  // bounds the offset carried
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) st.acc[dt] -= st.corr;
+    st.corr = 0.f;
   }
   if (kb + 1 < nkb) __builtin_amdgcn_s_waitcnt(0);  // the next block has landed in LDS
   lds_barrier();
@@ -302,6 +321,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
   RowState st;
   st.m_run = -INFINITY;
   st.l_part = 0.f;
+  st.corr = 0.f;
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) st.acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
 
@@ -320,8 +340,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) {
       float4 v;
-      v.x = st.acc[dt][0] * il; v.y = st.acc[dt][1] * il;
-      v.z = st.acc[dt][2] * il; v.w = st.acc[dt][3] * il;
+      v.x = (st.acc[dt][0] - st.corr) * il; v.y = (st.acc[dt][1] - st.corr) * il;
+      v.z = (st.acc[dt][2] - st.corr) * il; v.w = (st.acc[dt][3] - st.corr) * il;
       *reinterpret_cast<float4*>(o + 16 * dt) = v;
     }
   }

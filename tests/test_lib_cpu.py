@@ -126,6 +126,7 @@ def test_attn_prefill_validation():
     assert call(8, 2) == C["I8A_EINVAL"]               # causal flag
     assert call(7, 0) == C["I8A_EINVAL"]               # empty context
     assert call(14, None) == C["I8A_EINVAL"]           # out null
+    assert call(9, 1 << 26) == C["I8A_EUNSUPPORTED"]   # pool past the 32-bit scale index
     assert call(1, 0) == C["I8A_OK"]                   # no queries: no-op
 
 
