@@ -161,6 +161,31 @@ def decode_exact(q_codes, q_scales, cache_view, sm_scale):
                            np.array([ctx - 1]))[0]
 
 
+def verify_exact(q_codes, q_scales, cache_view, sm_scale):
+    """Exact multi-row decode (speculative / multi-token verify) for one sequence.
+
+    q_codes [nq,Hq,D] int8 and q_scales [nq,Hq] are the nq newest query rows; the
+    cache view (k_codes [ctx,Hkv,D], k_scales [ctx,Hkv], v_codes, v_scales) already
+    holds their K/V. Row i sits at position ctx - nq + i and sees keys 0 .. ctx - nq + i,
+    the causal rule of a chunk ("dot4-flash-attention" README: the MTP verify step
+    runs a few query rows at once and its next-steps list extends split-K decode to
+    such small query batches; vLLM docs page, "Row shape routing": speculative-verify
+    decode of a few rows runs on a multi-row kernel). A row with no visible key
+    (ctx < nq) gets zeros. Returns [nq,Hq,D] float64.
+    """
+    kc, ks, vc, vs = cache_view
+    nq = int(q_codes.shape[0])
+    ctx = int(kc.shape[0])
+    last = ctx - nq + np.arange(nq)
+    out = np.zeros((nq,) + tuple(q_codes.shape[1:]), dtype=np.float64)
+    live = last >= 0
+    if live.any():
+        qd = dequantize(q_codes[live], q_scales[live])
+        out[live] = attention_exact(qd, dequantize(kc, ks), dequantize(vc, vs), sm_scale,
+                                    last[live])
+    return out
+
+
 def brute_force_attention(qd, kd, vd, sm_scale, last_key):
     """Pure-Python triple loop, for tiny shapes only (the pin of attention_exact)."""
     R, Hq, D = len(qd), len(qd[0]), len(qd[0][0])

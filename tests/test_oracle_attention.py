@@ -108,6 +108,57 @@ def test_chunk_row_equals_decode_at_matching_context():
         assert np.max(np.abs(chunk[t] - dec[0])) <= 1e-13
 
 
+# ---- multi-row decode (verify) ----
+
+def _verify_case(seed, ctx, nq):
+    case = workloads.make_decode_case(seed, [ctx], pages="random", k_outliers=4, q_rows_per_seq=nq)
+    k, v, q, slots = case.all_data()
+    kc, ks = quant.quantize_rows(k); vc, vs = quant.quantize_rows(v)
+    qc, qs = quant.quantize_rows(quant.bf16_bits_to_f32(q[0]))
+    cache = paged.alloc_cache(case.num_pages, 4)
+    paged.write_rows(cache, slots, kc, ks, vc, vs)
+    return paged.gather_seq(cache, case.block_table[0], ctx, 4), qc, qs
+
+
+def test_verify_rows_equal_decode_at_their_own_context():
+    view, qc, qs = _verify_case(41, 37, 4)          # rows at positions 33..36, across a page edge
+    out = A.verify_exact(qc, qs, view, SM)
+    for i in range(4):
+        c_i = 37 - 4 + i + 1
+        trunc = tuple(a[:c_i] for a in view)
+        dec = A.decode_exact(qc[i], qs[i], trunc, SM)
+        assert np.max(np.abs(out[i] - dec)) <= 1e-13   # summation order only
+    assert not np.allclose(out[0], out[3])
+
+
+def test_verify_one_row_is_decode():
+    view, qc, qs = _verify_case(42, 50, 1)
+    assert np.array_equal(A.verify_exact(qc, qs, view, SM)[0], A.decode_exact(qc[0], qs[0], view, SM))
+
+
+def test_verify_matches_brute_force_tiny():
+    rng = np.random.default_rng(43)
+    N, nq, Hkv, Hq, D = 7, 3, 1, 2, 8
+    kc = rng.integers(-127, 128, (N, Hkv, D)).astype(np.int8); ks = rng.uniform(0.01, 0.03, (N, Hkv))
+    vc = rng.integers(-127, 128, (N, Hkv, D)).astype(np.int8); vs = rng.uniform(0.01, 0.03, (N, Hkv))
+    qc = rng.integers(-127, 128, (nq, Hq, D)).astype(np.int8); qs = rng.uniform(0.01, 0.03, (nq, Hq))
+    out = A.verify_exact(qc, qs, (kc, ks, vc, vs), 0.35)
+    ref = A.brute_force_attention(quant.dequantize(qc, qs).tolist(), quant.dequantize(kc, ks).tolist(),
+                                  quant.dequantize(vc, vs).tolist(), 0.35, [4, 5, 6])
+    assert np.max(np.abs(out - ref)) <= 1e-12
+
+
+def test_verify_rows_before_the_context_are_zero():
+    rng = np.random.default_rng(44)
+    kc = rng.integers(-127, 128, (2, 1, 8)).astype(np.int8); ks = np.array([[0.02], [0.03]])
+    vc = rng.integers(-127, 128, (2, 1, 8)).astype(np.int8); vs = np.array([[0.05], [0.07]])
+    qc = rng.integers(-127, 128, (4, 6, 8)).astype(np.int8); qs = np.full((4, 6), 0.02)
+    out = A.verify_exact(qc, qs, (kc, ks, vc, vs), SM)   # rows at positions -2, -1, 0, 1
+    assert np.all(out[:2] == 0.0)
+    vdeq = quant.dequantize(vc, vs)
+    assert np.array_equal(out[2], np.broadcast_to(vdeq[0, 0], (6, 8)))   # one key: V itself
+
+
 # ---- int8-P emulation (oracle B) ----
 
 def test_int8p_matches_brute_force():
