@@ -186,6 +186,25 @@ def verify_exact(q_codes, q_scales, cache_view, sm_scale):
     return out
 
 
+def verify_int8p(q_codes, q_scales, cache_view, sm_scale):
+    """Int8-P decode / verify for one sequence ("oracle B" rule of attention_int8p with
+    the verify visibility of verify_exact: row i of nq sees keys 0 .. ctx - nq + i; a row
+    with no visible key gets zeros). The 64-key blocks are aligned to key 0, so the
+    codes do not depend on how a kernel splits the keys ("INT8 KV and INT8 MMAC
+    attention on a gfx936 DCU", §3.3: decode with INT8 PV, weights quantized per block
+    with scale = block absmax / 127). Returns [nq,Hq,D] float64."""
+    kc, ks, vc, vs = cache_view
+    nq = int(q_codes.shape[0])
+    ctx = int(kc.shape[0])
+    last = ctx - nq + np.arange(nq)
+    out = np.zeros((nq,) + tuple(q_codes.shape[1:]), dtype=np.float64)
+    live = last >= 0
+    if live.any():
+        qd = dequantize(q_codes[live], q_scales[live])
+        out[live] = attention_int8p(qd, dequantize(kc, ks), vc, vs, sm_scale, last[live])
+    return out
+
+
 def brute_force_attention(qd, kd, vd, sm_scale, last_key):
     """Pure-Python triple loop, for tiny shapes only (the pin of attention_exact)."""
     R, Hq, D = len(qd), len(qd[0]), len(qd[0][0])

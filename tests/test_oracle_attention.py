@@ -159,6 +159,30 @@ def test_verify_rows_before_the_context_are_zero():
     assert np.array_equal(out[2], np.broadcast_to(vdeq[0, 0], (6, 8)))   # one key: V itself
 
 
+def test_verify_int8p_rows_equal_int8p_at_their_own_context():
+    view, qc, qs = _verify_case(45, 150, 3)         # rows at 147..149: the third 64-key block
+    out = A.verify_int8p(qc, qs, view, SM)
+    kc, ks, vc, vs = view
+    for i in range(3):
+        c_i = 150 - 3 + i + 1
+        ref = A.attention_int8p(quant.dequantize(qc[i:i + 1], qs[i:i + 1]),
+                                quant.dequantize(kc[:c_i], ks[:c_i]), vc[:c_i], vs[:c_i], SM,
+                                [c_i - 1])[0]
+        assert np.max(np.abs(out[i] - ref)) <= 1e-13
+
+
+def test_verify_int8p_matches_brute_force_tiny():
+    rng = np.random.default_rng(46)
+    N, nq, D = 70, 2, 8                               # crosses one 64-key block edge
+    kc = rng.integers(-127, 128, (N, 1, D)).astype(np.int8); ks = rng.uniform(0.01, 0.03, (N, 1))
+    vc = rng.integers(-127, 128, (N, 1, D)).astype(np.int8); vs = rng.uniform(0.01, 0.03, (N, 1))
+    qc = rng.integers(-127, 128, (nq, 2, D)).astype(np.int8); qs = rng.uniform(0.01, 0.03, (nq, 2))
+    out = A.verify_int8p(qc, qs, (kc, ks, vc, vs), 0.35)
+    ref = A.brute_force_int8p(quant.dequantize(qc, qs).tolist(), quant.dequantize(kc, ks).tolist(),
+                              vc.tolist(), vs.tolist(), 0.35, [N - 2, N - 1])
+    assert np.max(np.abs(out - ref)) <= 1e-12
+
+
 # ---- int8-P emulation (oracle B) ----
 
 def test_int8p_matches_brute_force():
