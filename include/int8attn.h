@@ -155,6 +155,85 @@ int attn_decode(const uint16_t* q,
                 float sm_scale, float* out,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of scratch attn_verify needs: num_seqs * nq * n_q_heads *
+ * ceil(max_context_len/512) * (2 + head_dim) floats, rounded up to 256 bytes (nq = 1:
+ * the same as attn_decode_workspace_bytes). Returns 0 for invalid arguments. */
+size_t attn_verify_workspace_bytes(int num_seqs, int nq, int max_context_len,
+                                   int n_q_heads, int head_dim);
+
+/* attn_verify -- nq (1..8) new query rows per sequence against its paged INT8 K/V
+ * (speculative / multi-token verify, small-batch decode).
+ * [DOT4 README: the MTP verify step runs a few query rows and the next steps extend
+ *  split-K decode to such small query batches; R4D "Row shape routing": verify rows go
+ *  to a multi-row kernel that reads each K/V tile once for all rows, one row to the
+ *  one-row kernel; causal rule of a chunk as in attn_prefill_chunk.]
+ *
+ *  Same two stages and the same 512-row partitions as attn_decode; each (sequence, KV
+ *  head, partition) workgroup reads its K/V once for all 6 * nq query rows of the group.
+ *  nq == 1 runs the attn_decode kernels (identical results). For nq >= 2 the weighted
+ *  sum of V runs on the int8 matrix cores with each weight w / s_b (s_b = block max /
+ *  127, aligned 64-key blocks) carried as three 7-bit digit planes, i.e. to 2^-15 of
+ *  s_b, which keeps the fp32-class bound of attn_decode.
+ *  q             bf16 [num_seqs][nq][n_q_heads][head_dim]; query i of sequence s sits
+ *                at position ctx_s - nq + i and sees keys 0 .. ctx_s - nq + i (its own
+ *                and the earlier new rows' K/V must already be written).
+ *  context_lens  int32 [num_seqs], clamped like attn_decode's; a query row with no
+ *                visible key (ctx_s < nq) produces zeros.
+ *  out           fp32 [num_seqs][nq][n_q_heads][head_dim], fully overwritten.
+ *  workspace     >= attn_verify_workspace_bytes(...) bytes.
+ *  Other arguments as for attn_decode. nq outside 1..8 or num_seqs * nq > 65535
+ *  returns I8A_EINVAL. */
+int attn_verify(const uint16_t* q, int nq,
+                const int8_t* k_cache, const int8_t* v_cache,
+                const float* k_scale, const float* v_scale,
+                const int32_t* block_table, int max_blocks_per_seq,
+                const int32_t* context_lens, int num_seqs, int max_context_len,
+                int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                float sm_scale, float* out,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Keys per split-K partition that attn_decode_int8p uses when passed partition_rows = 0:
+ * 512 when max_context_len <= 512 (one partition: the workgroup writes the output and no
+ * merge stage runs); otherwise the largest of 512, 256, 128 for which num_seqs *
+ * n_kv_heads * ceil(max_context_len / partition) reaches 64 workgroups, else 128
+ * [R4D "The selection law": a power-of-two segment count from a workgroup-count target
+ * over (KV heads x rows), with a floor on keys per segment; DCU §3.3: 256-token decode
+ * partitions]. Returns 0 for invalid arguments. */
+int attn_decode_partition_rows(int num_seqs, int max_context_len, int n_kv_heads);
+
+/* Bytes of scratch attn_decode_int8p needs: num_seqs * nq * n_q_heads *
+ * ceil(max_context_len / partition) * (2 + head_dim) floats, rounded up to 256 bytes,
+ * with the partition resolved as attn_decode_int8p resolves it. 0 for invalid
+ * arguments. */
+size_t attn_decode_int8p_workspace_bytes(int num_seqs, int nq, int max_context_len,
+                                         int n_q_heads, int n_kv_heads, int head_dim,
+                                         int partition_rows);
+
+/* attn_decode_int8p -- decode / verify with int8 softmax weights: the int8-P variant of
+ * attn_verify (nq = 1: decode).
+ * [DCU §3.3: the decode kernel's INT8 PV, the V scale folded into the weight, weights
+ *  quantized per block with scale = block absmax / 127 and the block's int8 product
+ *  scaled back by it; 256-token partitions; R4D "The selection law".]
+ *
+ *  As attn_verify, except: the weights p * sV of each query row and aligned 64-key
+ *  block are carried as int8 codes rint(w / s_b), s_b = max_block(w) / 127, multiplied
+ *  with the V codes on the int8 matrix cores (the same rule as attn_prefill_chunk; the
+ *  denominator sums the unquantized weights), and the partition size is
+ *  partition_rows keys (64, 128, 256 or 512; 0 = attn_decode_partition_rows). The
+ *  codes of a key do not depend on the partition, so neither does the result beyond
+ *  rounding.
+ *  workspace     >= attn_decode_int8p_workspace_bytes(...) with the same partition_rows.
+ *  Other arguments as for attn_verify; a partition_rows value outside the list returns
+ *  I8A_EINVAL. */
+int attn_decode_int8p(const uint16_t* q, int nq,
+                      const int8_t* k_cache, const int8_t* v_cache,
+                      const float* k_scale, const float* v_scale,
+                      const int32_t* block_table, int max_blocks_per_seq,
+                      const int32_t* context_lens, int num_seqs, int max_context_len,
+                      int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                      int partition_rows, float sm_scale, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* attn_prefill_chunk -- n_new query tokens at the tail of one sequence, one pass.
  * [DCU §3.2: INT8 Q with history and current INT8 K/V in one online-softmax pass, INT8
  *  QK, INT8 PV; DCU §3.3 and §1.3: the V scale is folded into the softmax weight, the

@@ -16,7 +16,9 @@ import os
 import torch
 
 __all__ = ["lib", "PagedCache", "alloc_cache", "kv_quant_write", "q_quant", "attn_decode",
-           "attn_decode_workspace_bytes", "attn_prefill_chunk", "Int8AttnError",
+           "attn_decode_workspace_bytes", "attn_verify", "attn_verify_workspace_bytes",
+           "attn_decode_int8p", "attn_decode_int8p_workspace_bytes", "attn_decode_partition_rows",
+           "attn_prefill_chunk", "Int8AttnError",
            "HEAD_DIM", "PAGE", "PARTITION", "EXPORTED_SYMBOLS"]
 
 HEAD_DIM = 256
@@ -24,7 +26,10 @@ PAGE = 16
 PARTITION = 512
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint8attn.so")
 EXPORTED_SYMBOLS = ("int8attn_last_error", "int8attn_version", "kv_quant_write", "q_quant",
-                    "attn_decode_workspace_bytes", "attn_decode", "attn_prefill_chunk")
+                    "attn_decode_workspace_bytes", "attn_decode", "attn_verify_workspace_bytes",
+                    "attn_verify", "attn_decode_partition_rows",
+                    "attn_decode_int8p_workspace_bytes", "attn_decode_int8p",
+                    "attn_prefill_chunk")
 
 _c_void = ctypes.c_void_p
 _c_int = ctypes.c_int
@@ -41,6 +46,16 @@ _SIGNATURES = {
     "attn_decode": (_c_int, [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void, _c_int,
                              _c_void, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
                              _c_void, _c_void, _c_size, _c_void]),
+    "attn_verify_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "attn_verify": (_c_int, [_c_void, _c_int, _c_void, _c_void, _c_void, _c_void, _c_void, _c_int,
+                             _c_void, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                             _c_void, _c_void, _c_size, _c_void]),
+    "attn_decode_partition_rows": (_c_int, [_c_int, _c_int, _c_int]),
+    "attn_decode_int8p_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                                    _c_int]),
+    "attn_decode_int8p": (_c_int, [_c_void, _c_int, _c_void, _c_void, _c_void, _c_void, _c_void,
+                                   _c_int, _c_void, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                   _c_int, _c_float, _c_void, _c_void, _c_size, _c_void]),
     "attn_prefill_chunk": (_c_int, [_c_void, _c_int, _c_void, _c_void, _c_void, _c_void,
                                     _c_void, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     _c_float, _c_void, _c_void]),
@@ -185,6 +200,82 @@ def attn_decode(q: torch.Tensor, cache, block_table: torch.Tensor, context_lens:
                              int(max_context_len), cache.num_pages, Hq, cache.n_kv_heads, D, sm,
                              _dev(out, "out", torch.float32), _dev(workspace, "workspace"),
                              workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def attn_verify_workspace_bytes(num_seqs: int, nq: int, max_context_len: int, n_q_heads: int,
+                                head_dim: int = HEAD_DIM) -> int:
+    return int(lib().attn_verify_workspace_bytes(num_seqs, nq, max_context_len, n_q_heads, head_dim))
+
+
+def attn_verify(q: torch.Tensor, cache, block_table: torch.Tensor, context_lens: torch.Tensor,
+                max_context_len: int, sm_scale: float | None = None, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Multi-row decode: q bf16 [S, nq, Hq, 256] (query i of a sequence at position
+    ctx - nq + i) -> out fp32 [S, nq, Hq, 256] over the paged INT8 cache."""
+    if q.dtype != torch.bfloat16 or q.dim() != 4:
+        raise TypeError("q must be bfloat16 [S, nq, Hq, head_dim]")
+    S, nq, Hq, D = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != S:
+        raise ValueError("block_table must be [S, max_blocks]")
+    if context_lens.shape != (S,):
+        raise ValueError("context_lens must be [S]")
+    if out is None:
+        out = torch.empty((S, nq, Hq, D), dtype=torch.float32, device=q.device)
+    need = attn_verify_workspace_bytes(S, nq, max_context_len, Hq, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    sm = float(sm_scale if sm_scale is not None else D ** -0.5)
+    _check(lib().attn_verify(_dev(q, "q"), nq, *cache.ptrs(),
+                             _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+                             _dev(context_lens, "context_lens", torch.int32), S,
+                             int(max_context_len), cache.num_pages, Hq, cache.n_kv_heads, D, sm,
+                             _dev(out, "out", torch.float32), _dev(workspace, "workspace"),
+                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def attn_decode_partition_rows(num_seqs: int, max_context_len: int, n_kv_heads: int) -> int:
+    return int(lib().attn_decode_partition_rows(num_seqs, max_context_len, n_kv_heads))
+
+
+def attn_decode_int8p_workspace_bytes(num_seqs: int, nq: int, max_context_len: int,
+                                      n_q_heads: int, n_kv_heads: int, head_dim: int = HEAD_DIM,
+                                      partition_rows: int = 0) -> int:
+    return int(lib().attn_decode_int8p_workspace_bytes(num_seqs, nq, max_context_len, n_q_heads,
+                                                       n_kv_heads, head_dim, partition_rows))
+
+
+def attn_decode_int8p(q: torch.Tensor, cache, block_table: torch.Tensor,
+                      context_lens: torch.Tensor, max_context_len: int, partition_rows: int = 0,
+                      sm_scale: float | None = None, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Int8-P decode/verify: q bf16 [S, Hq, 256] (one row) or [S, nq, Hq, 256] -> out fp32
+    of the same shape."""
+    if q.dtype != torch.bfloat16 or q.dim() not in (3, 4):
+        raise TypeError("q must be bfloat16 [S, Hq, head_dim] or [S, nq, Hq, head_dim]")
+    one_row = q.dim() == 3
+    q4 = q.unsqueeze(1) if one_row else q
+    S, nq, Hq, D = q4.shape
+    if block_table.dim() != 2 or block_table.shape[0] != S:
+        raise ValueError("block_table must be [S, max_blocks]")
+    if context_lens.shape != (S,):
+        raise ValueError("context_lens must be [S]")
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
+    need = attn_decode_int8p_workspace_bytes(S, nq, max_context_len, Hq, cache.n_kv_heads, D,
+                                             partition_rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    sm = float(sm_scale if sm_scale is not None else D ** -0.5)
+    _check(lib().attn_decode_int8p(_dev(q4, "q"), nq, *cache.ptrs(),
+                                   _dev(block_table, "block_table", torch.int32),
+                                   block_table.shape[1],
+                                   _dev(context_lens, "context_lens", torch.int32), S,
+                                   int(max_context_len), cache.num_pages, Hq, cache.n_kv_heads, D,
+                                   int(partition_rows), sm, _dev(out, "out", torch.float32),
+                                   _dev(workspace, "workspace"),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

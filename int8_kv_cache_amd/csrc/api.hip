@@ -46,6 +46,28 @@ static size_t decode_ws_bytes(long long num_seqs, long long max_ctx, long long n
   return (size_t)((floats * 4 + 255) / 256 * 256);
 }
 
+// Keys per split-K partition of the int8-PV decode when the caller passes 0. The vLLM
+// docs page's selection law picks a power-of-two segment count from a workgroup-count
+// target over (KV heads x rows) with a floor on keys per segment; in this kernel every
+// wave owns one 64-key block whatever the partition size, so smaller partitions add
+// partials (merge work) without adding waves, and only help by spreading a short grid
+// over more CUs. Hence: a context that fits one partition takes 512 keys (one
+// partition, no merge stage); otherwise halve from 512 while sequences x KV heads x
+// partitions stays under 64 workgroups, down to 128 keys.
+static int partition_law(long long num_seqs, long long max_ctx, long long n_kv_heads) {
+  constexpr long long kTargetWorkgroups = 64;
+  if (max_ctx <= 512) return 512;
+  int p = 512;
+  while (p > 128 && num_seqs * n_kv_heads * ((max_ctx + p - 1) / p) < kTargetWorkgroups) p >>= 1;
+  return p;
+}
+
+static size_t partials_bytes(long long rows, long long max_ctx, long long n_q_heads, int part) {
+  const long long parts = (max_ctx + part - 1) / part;
+  const long long floats = rows * n_q_heads * parts * (2 + 256);
+  return (size_t)((floats * 4 + 255) / 256 * 256);
+}
+
 }  // namespace i8a
 
 using namespace i8a;
@@ -115,6 +137,99 @@ int attn_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cache,
   return launch_decode(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks_per_seq,
                        context_lens, num_seqs, max_context_len, num_pages, n_q_heads, n_kv_heads,
                        sm_scale, out, (float*)workspace, max_parts, (hipStream_t)stream);
+}
+
+size_t attn_verify_workspace_bytes(int num_seqs, int nq, int max_context_len, int n_q_heads,
+                                   int head_dim) {
+  if (num_seqs <= 0 || nq < 1 || nq > 8 || max_context_len <= 0 || n_q_heads <= 0 || head_dim != 256)
+    return 0;
+  return decode_ws_bytes((long long)num_seqs * nq, max_context_len, n_q_heads);
+}
+
+int attn_verify(const uint16_t* q, int nq, const int8_t* k_cache, const int8_t* v_cache,
+                const float* k_scale, const float* v_scale, const int32_t* block_table,
+                int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                int max_context_len, int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
+  if (rc) return rc;
+  if (nq < 1 || nq > 8) return set_error(I8A_EINVAL, "attn_verify: nq %d outside 1..8", nq);
+  if (num_seqs < 0 || (long long)num_seqs * nq > 65535)
+    return set_error(I8A_EINVAL, "attn_verify: num_seqs %d x nq %d", num_seqs, nq);
+  if (num_seqs == 0) return I8A_OK;
+  if (max_context_len <= 0 || max_blocks_per_seq <= 0 || num_pages <= 0)
+    return set_error(I8A_EINVAL, "attn_verify: max_context_len %d, max_blocks_per_seq %d, num_pages %d",
+                     max_context_len, max_blocks_per_seq, num_pages);
+  if (!isfinite(sm_scale)) return set_error(I8A_EINVAL, "attn_verify: sm_scale not finite");
+  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_table || !context_lens || !out ||
+      !workspace)
+    return set_error(I8A_EINVAL, "attn_verify: null pointer");
+  if (((uintptr_t)workspace & 15u) != 0) return set_error(I8A_EINVAL, "attn_verify: workspace not 16-byte aligned");
+  const size_t need = decode_ws_bytes((long long)num_seqs * nq, max_context_len, n_q_heads);
+  if (workspace_bytes < need)
+    return set_error(I8A_EWORKSPACE, "attn_verify: workspace %zu bytes < %zu needed", workspace_bytes, need);
+  const int max_parts = (max_context_len + 511) / 512;
+  return launch_verify(q, nq, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks_per_seq,
+                       context_lens, num_seqs, max_context_len, num_pages, n_q_heads, n_kv_heads,
+                       sm_scale, out, (float*)workspace, max_parts, (hipStream_t)stream);
+}
+
+int attn_decode_partition_rows(int num_seqs, int max_context_len, int n_kv_heads) {
+  if (num_seqs <= 0 || max_context_len <= 0 || n_kv_heads <= 0) return 0;
+  return partition_law(num_seqs, max_context_len, n_kv_heads);
+}
+
+static int resolve_partition(int partition_rows, int num_seqs, int max_context_len, int n_kv_heads) {
+  if (partition_rows == 0) return partition_law(num_seqs, max_context_len, n_kv_heads);
+  if (partition_rows == 64 || partition_rows == 128 || partition_rows == 256 || partition_rows == 512)
+    return partition_rows;
+  return -1;
+}
+
+size_t attn_decode_int8p_workspace_bytes(int num_seqs, int nq, int max_context_len, int n_q_heads,
+                                         int n_kv_heads, int head_dim, int partition_rows) {
+  if (num_seqs <= 0 || nq < 1 || nq > 8 || max_context_len <= 0 || n_q_heads <= 0 ||
+      n_kv_heads <= 0 || head_dim != 256)
+    return 0;
+  const int part = resolve_partition(partition_rows, num_seqs, max_context_len, n_kv_heads);
+  if (part < 0) return 0;
+  return partials_bytes((long long)num_seqs * nq, max_context_len, n_q_heads, part);
+}
+
+int attn_decode_int8p(const uint16_t* q, int nq, const int8_t* k_cache, const int8_t* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* block_table,
+                      int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                      int max_context_len, int num_pages, int n_q_heads, int n_kv_heads,
+                      int head_dim, int partition_rows, float sm_scale, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
+  if (rc) return rc;
+  if (nq < 1 || nq > 8) return set_error(I8A_EINVAL, "attn_decode_int8p: nq %d outside 1..8", nq);
+  if (num_seqs < 0 || (long long)num_seqs * nq > 65535)
+    return set_error(I8A_EINVAL, "attn_decode_int8p: num_seqs %d x nq %d", num_seqs, nq);
+  if (num_seqs == 0) return I8A_OK;
+  if (max_context_len <= 0 || max_blocks_per_seq <= 0 || num_pages <= 0)
+    return set_error(I8A_EINVAL, "attn_decode_int8p: max_context_len %d, max_blocks_per_seq %d, num_pages %d",
+                     max_context_len, max_blocks_per_seq, num_pages);
+  const int part = resolve_partition(partition_rows, num_seqs, max_context_len, n_kv_heads);
+  if (part < 0)
+    return set_error(I8A_EINVAL, "attn_decode_int8p: partition_rows %d (0, 64, 128, 256 or 512)",
+                     partition_rows);
+  if (!isfinite(sm_scale)) return set_error(I8A_EINVAL, "attn_decode_int8p: sm_scale not finite");
+  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_table || !context_lens || !out ||
+      !workspace)
+    return set_error(I8A_EINVAL, "attn_decode_int8p: null pointer");
+  if (((uintptr_t)workspace & 15u) != 0)
+    return set_error(I8A_EINVAL, "attn_decode_int8p: workspace not 16-byte aligned");
+  const size_t need = partials_bytes((long long)num_seqs * nq, max_context_len, n_q_heads, part);
+  if (workspace_bytes < need)
+    return set_error(I8A_EWORKSPACE, "attn_decode_int8p: workspace %zu bytes < %zu needed",
+                     workspace_bytes, need);
+  return launch_decode_i8pv(1, part, q, nq, k_cache, v_cache, k_scale, v_scale, block_table,
+                            max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_pages,
+                            n_q_heads, n_kv_heads, sm_scale, out, (float*)workspace,
+                            (hipStream_t)stream);
 }
 
 int attn_prefill_chunk(const uint16_t* q, int n_new, const int8_t* k_cache, const int8_t* v_cache,

@@ -41,7 +41,9 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ ctx_lens, int ctx_cap, int num_pages, int n_q_heads,
     int n_kv_heads, float qk_scale_log2, float* __restrict__ ws_m, float* __restrict__ ws_l,
-    float* __restrict__ ws_o, int max_parts) {
+    float* __restrict__ ws_o, int max_parts, float* __restrict__ out) {
+  // out != nullptr: a single partition per sequence, so the workgroup writes the
+  // normalized output itself and no merge stage runs.
   const int j = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -58,7 +60,12 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
   asm volatile("" ::"s"(ctx), "s"(pr[0]), "s"(pr[1]), "s"(pr[2]), "s"(pr[3]));
   ctx = ctx < 0 ? 0 : (ctx > ctx_cap ? ctx_cap : ctx);
   const int tok0 = j * kPart;
-  if (tok0 >= ctx) return;  // whole workgroup: this partition is past the context
+  if (tok0 >= ctx) {  // whole workgroup: this partition is past the context
+    if (out != nullptr)  // no key at all: zeros
+      for (int i = tid; i < kGroup * kHeadDim; i += 512)
+        out[((size_t)s * n_q_heads + g * kGroup) * kHeadDim + i] = 0.f;
+    return;
+  }
   const int n_tok = min(kPart, ctx - tok0);
 
   __shared__ __align__(16) int8_t s_q[kGroup][kHeadDim];
@@ -269,6 +276,11 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
       const float4 ov = *reinterpret_cast<const float4*>(&s_o[ww][h][4 * lane]);
       acc.x += af * ov.x; acc.y += af * ov.y; acc.z += af * ov.z; acc.w += af * ov.w;
     }
+    if (out != nullptr) {
+      *reinterpret_cast<float4*>(&out[((size_t)s * n_q_heads + g * kGroup + h) * kHeadDim + 4 * lane]) =
+          make_float4(acc.x / L, acc.y / L, acc.z / L, acc.w / L);
+      return;
+    }
     const size_t pi = ((size_t)s * n_q_heads + g * kGroup + h) * max_parts + j;
     *reinterpret_cast<float4*>(&ws_o[pi * kHeadDim + 4 * lane]) = acc;
     if (lane == 0) {
@@ -278,20 +290,22 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
   }
 }
 
-// Stage 2: one wave per (64-dim chunk, q head, sequence), online log-sum-exp over the
+// Stage 2: one wave per (64-dim chunk, q head, query row), online log-sum-exp over the
 // partitions in chunks of 64: lane j holds m_j and l_j, every lane loads o_j[d] of all
 // 64 partitions of the chunk up front. The first chunk is loaded together with the
 // context length (indices clamped to the workspace), so a call with at most 64
-// partitions costs one memory round trip.
+// partitions costs one memory round trip. Query row z is query i = z % nq of sequence
+// s = z / nq and sees ctx - nq + i + 1 keys (nq = 1: one row per sequence).
 // out = sum_j o_j 2^(m_j - M) / sum_j l_j 2^(m_j - M), M = max_j m_j.
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     const float* __restrict__ ws_m, const float* __restrict__ ws_l, const float* __restrict__ ws_o,
-    const int32_t* __restrict__ ctx_lens, int ctx_cap, int n_q_heads, int max_parts,
-    float* __restrict__ out) {
-  const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+    const int32_t* __restrict__ ctx_lens, int ctx_cap, int n_q_heads, int max_parts, int nq,
+    int part_rows, float* __restrict__ out) {
+  const int c = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
+  const int s = z / nq, qi = z - s * nq;
   const int lane = threadIdx.x;
   const int d = c * 64 + lane;
-  const size_t base = ((size_t)s * n_q_heads + h) * max_parts;
+  const size_t base = ((size_t)z * n_q_heads + h) * max_parts;
   const float* pm = ws_m + base;
   const float* pl = ws_l + base;
   const float* po = ws_o + base * kHeadDim + d;
@@ -306,8 +320,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   int ctx = ctx_lens[s];
   load_chunk(0, min(64, max_parts));
   ctx = ctx < 0 ? 0 : (ctx > ctx_cap ? ctx_cap : ctx);
-  const int P = (ctx + kPart - 1) / kPart;
-  float* o = out + ((size_t)s * n_q_heads + h) * kHeadDim;
+  const int keys = max(0, ctx - nq + qi + 1);  // keys this query row sees
+  const int P = (keys + part_rows - 1) / part_rows;
+  float* o = out + ((size_t)z * n_q_heads + h) * kHeadDim;
   if (P == 0) {
     o[d] = 0.f;
     return;
@@ -356,12 +371,37 @@ int launch_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cach
   hipLaunchKernelGGL(decode_split_kernel, dim3(max_parts, n_kv_heads, num_seqs), dim3(512), 0,
                      stream, q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks,
                      ctx_lens, ctx_cap, num_pages, n_q_heads, n_kv_heads, sm_scale * kLog2e, ws_m,
-                     ws_l, ws_o, max_parts);
+                     ws_l, ws_o, max_parts, max_parts == 1 ? out : nullptr);
   int rc = check_launch("attn_decode stage 1");
-  if (rc) return rc;
+  if (rc || max_parts == 1) return rc;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(kHeadDim / 64, n_q_heads, num_seqs), dim3(64), 0,
-                     stream, ws_m, ws_l, ws_o, ctx_lens, ctx_cap, n_q_heads, max_parts, out);
+                     stream, ws_m, ws_l, ws_o, ctx_lens, ctx_cap, n_q_heads, max_parts, 1, kPart, out);
   return check_launch("attn_decode stage 2");
+}
+
+int launch_verify(const uint16_t* q, int nq, const int8_t* k_cache, const int8_t* v_cache,
+                  const float* k_scale, const float* v_scale, const int32_t* block_table,
+                  int max_blocks, const int32_t* ctx_lens, int num_seqs, int max_ctx,
+                  int num_pages, int n_q_heads, int n_kv_heads, float sm_scale, float* out,
+                  float* ws, int max_parts, hipStream_t stream) {
+  if (nq == 1)  // one row: the one-row kernel (route by live rows)
+    return launch_decode(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, ctx_lens,
+                         num_seqs, max_ctx, num_pages, n_q_heads, n_kv_heads, sm_scale, out, ws,
+                         max_parts, stream);
+  // several rows: one read of the K/V for all of them, the weighted sum of V on the int8
+  // matrix cores with three digit planes per weight
+  return launch_decode_i8pv(3, kPart, q, nq, k_cache, v_cache, k_scale, v_scale, block_table,
+                            max_blocks, ctx_lens, num_seqs, max_ctx, num_pages, n_q_heads,
+                            n_kv_heads, sm_scale, out, ws, stream);
+}
+
+int launch_merge(const float* ws_m, const float* ws_l, const float* ws_o, const int32_t* ctx_lens,
+                 int ctx_cap, int num_seqs, int nq, int n_q_heads, int max_parts, int part_rows,
+                 float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(kHeadDim / 64, n_q_heads, num_seqs * nq), dim3(64),
+                     0, stream, ws_m, ws_l, ws_o, ctx_lens, ctx_cap, n_q_heads, max_parts, nq,
+                     part_rows, out);
+  return check_launch("decode merge");
 }
 
 }  // namespace i8a

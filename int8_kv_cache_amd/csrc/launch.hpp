@@ -21,6 +21,19 @@ int launch_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cach
                   int max_blocks, const int32_t* ctx_lens, int num_seqs, int max_ctx,
                   int num_pages, int n_q_heads, int n_kv_heads, float sm_scale, float* out,
                   float* ws, int max_parts, hipStream_t stream);
+int launch_verify(const uint16_t* q, int nq, const int8_t* k_cache, const int8_t* v_cache,
+                  const float* k_scale, const float* v_scale, const int32_t* block_table,
+                  int max_blocks, const int32_t* ctx_lens, int num_seqs, int max_ctx,
+                  int num_pages, int n_q_heads, int n_kv_heads, float sm_scale, float* out,
+                  float* ws, int max_parts, hipStream_t stream);
+int launch_merge(const float* ws_m, const float* ws_l, const float* ws_o, const int32_t* ctx_lens,
+                 int ctx_cap, int num_seqs, int nq, int n_q_heads, int max_parts, int part_rows,
+                 float* out, hipStream_t stream);
+int launch_decode_i8pv(int digits, int part_rows, const uint16_t* q, int nq, const int8_t* k_cache,
+                       const int8_t* v_cache, const float* k_scale, const float* v_scale,
+                       const int32_t* block_table, int max_blocks, const int32_t* ctx_lens,
+                       int num_seqs, int max_ctx, int num_pages, int n_q_heads, int n_kv_heads,
+                       float sm_scale, float* out, float* ws, hipStream_t stream);
 int launch_prefill(const uint16_t* q, int n_new, const int8_t* k_cache, const int8_t* v_cache,
                    const float* k_scale, const float* v_scale, const int32_t* block_table,
                    int ctx, int causal, int num_pages, int n_q_heads, int n_kv_heads,

@@ -59,7 +59,8 @@ class DecodeSetup:
         self.cache = gpu_cache(case.num_pages, H)
         keep = set(range(case.num_seqs)) if keep is None else set(keep)
         self.ref = {}
-        self.q_bits = np.zeros((case.num_seqs, case.n_q_heads, case.head_dim), np.uint16)
+        nq = case.q_rows_per_seq
+        self.q_rows = np.zeros((case.num_seqs, nq, case.n_q_heads, case.head_dim), np.uint16)
         self.vmax = 0.0
 
         def gen(s):
@@ -72,12 +73,14 @@ class DecodeSetup:
                 lib.kv_quant_write(up(k), up(v), up(slots), self.cache)
                 vc, vs = quant.quantize_rows(v)
                 self.vmax = max(self.vmax, float(np.max(np.abs(quant.dequantize(vc, vs)))))
-                self.q_bits[s] = q[0]
+                self.q_rows[s] = q
                 if s in keep:
                     kc, ks = quant.quantize_rows(k)
                     self.ref[s] = (kc, ks, vc, vs)
         torch.cuda.synchronize()
-        self.q = bf16_tensor(self.q_bits)
+        self.q_bits = self.q_rows[:, 0]
+        self.q = bf16_tensor(self.q_bits)          # first query row of each sequence
+        self.q_all = bf16_tensor(self.q_rows)      # [S, nq, Hq, D]
         self.table = up(case.block_table)
         self.ctx = up(case.context_lens)
 
@@ -87,6 +90,26 @@ class DecodeSetup:
 
     def run(self, **kw):
         out = lib.attn_decode(self.q, self.cache, self.table, self.ctx,
+                              int(self.case.max_context_len), **kw)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def oracle_verify(self, s, sm_scale=1.0 / 16):
+        qc, qs = quant.quantize_rows(quant.bf16_bits_to_f32(self.q_rows[s]))
+        return attention.verify_exact(qc, qs, self.ref[s], sm_scale)
+
+    def oracle_int8p(self, s, sm_scale=1.0 / 16):
+        qc, qs = quant.quantize_rows(quant.bf16_bits_to_f32(self.q_rows[s]))
+        return attention.verify_int8p(qc, qs, self.ref[s], sm_scale)
+
+    def run_int8p(self, **kw):
+        out = lib.attn_decode_int8p(self.q_all, self.cache, self.table, self.ctx,
+                                    int(self.case.max_context_len), **kw)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def run_verify(self, **kw):
+        out = lib.attn_verify(self.q_all, self.cache, self.table, self.ctx,
                               int(self.case.max_context_len), **kw)
         torch.cuda.synchronize()
         return out.cpu().numpy()

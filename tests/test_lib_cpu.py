@@ -110,6 +110,68 @@ def test_attn_decode_validation():
     assert call(8, 0) == C["I8A_OK"]                   # no sequences: no-op
 
 
+def test_attn_verify_validation():
+    C = _codes()
+    L = m.lib()
+    ws = m.attn_verify_workspace_bytes(2, 4, 1000, 24)
+    assert ws == m.attn_decode_workspace_bytes(8, 1000, 24)
+    assert m.attn_verify_workspace_bytes(2, 1, 1000, 24) == m.attn_decode_workspace_bytes(2, 1000, 24)
+    assert m.attn_verify_workspace_bytes(2, 9, 1000, 24) == 0
+    base = [FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 63, FAKE, 2, 1000, 200, 24, 4, 256, 0.0625,
+            FAKE, FAKE, ws, None]
+
+    def call(i=None, val=None):
+        a = list(base)
+        if i is not None:
+            a[i] = val
+        return L.attn_verify(*a)
+
+    assert call(1, 0) == C["I8A_EINVAL"]                # nq < 1
+    assert call(1, 9) == C["I8A_EINVAL"]                # nq > 8
+    assert call(9, 20000) == C["I8A_EINVAL"]            # num_seqs * nq > 65535
+    assert call(12, 12) == C["I8A_EUNSUPPORTED"]        # 12 q heads over 4 kv heads
+    assert call(18, ws - 1) == C["I8A_EWORKSPACE"]
+    assert call(16, None) == C["I8A_EINVAL"]            # out null
+    assert call(9, 0) == C["I8A_OK"]                    # no sequences: no-op
+
+
+def test_partition_law():
+    law = m.attn_decode_partition_rows
+    assert law(1, 256, 4) == 512        # one partition: no merge stage
+    assert law(1, 512, 4) == 512
+    assert law(1, 32768, 4) == 512      # 4 x 64 = 256 workgroups
+    assert law(1, 8192, 4) == 512       # 4 x 16 = 64
+    assert law(1, 4096, 4) == 256       # 4 x 8 = 32 -> 4 x 16 = 64
+    assert law(1, 3328, 4) == 128       # 28 -> 52 -> 104
+    assert law(1, 600, 4) == 128        # the 128-key floor
+    assert law(64, 1024, 4) == 512
+    assert law(0, 100, 4) == 0 and law(1, 0, 4) == 0
+
+
+def test_attn_decode_int8p_validation():
+    C = _codes()
+    L = m.lib()
+    ws = m.attn_decode_int8p_workspace_bytes(2, 1, 1000, 24, 4, partition_rows=64)
+    assert ws == m.attn_decode_workspace_bytes(2, 1000 * 8, 24)   # 16 partials of 64 keys
+    assert m.attn_decode_int8p_workspace_bytes(2, 1, 1000, 24, 4, partition_rows=0) == \
+        m.attn_decode_workspace_bytes(2, 1000 * 4, 24)            # law: 128 (8 partials)
+    assert m.attn_decode_int8p_workspace_bytes(2, 1, 1000, 24, 4, partition_rows=96) == 0
+    base = [FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 63, FAKE, 2, 1000, 200, 24, 4, 256, 64, 0.0625,
+            FAKE, FAKE, ws, None]
+
+    def call(i=None, val=None):
+        a = list(base)
+        if i is not None:
+            a[i] = val
+        return L.attn_decode_int8p(*a)
+
+    assert call(15, 96) == C["I8A_EINVAL"]              # partition size not in the list
+    assert call(1, 9) == C["I8A_EINVAL"]                # nq > 8
+    assert call(12, 18) == C["I8A_EUNSUPPORTED"]        # GQA group of 4.5
+    assert call(19, ws - 1) == C["I8A_EWORKSPACE"]
+    assert call(9, 0) == C["I8A_OK"]
+
+
 def test_attn_prefill_validation():
     C = _codes()
     L = m.lib()
