@@ -262,6 +262,40 @@ def main():
                             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "per_launch": dec_b,
                             "traffic": recorded_traffic("decode")},
     }
+    # ---- the next rows on the same caches (not part of the step): multi-row verify
+    # (nq query rows per sequence, fp32-class weights) and the int8-P decode, each timed
+    # as groups of back-to-back calls over the MALL-cold copies.
+    def group_us(fn, reps=10):
+        for c in copies:
+            fn(c)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            for c in copies:
+                fn(c)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * len(copies))
+
+    rng = np.random.default_rng(11)
+    verify = {}
+    for nq in (2, 4, 8):
+        qv = bf16(workloads.f32_to_bf16_bits(
+            rng.standard_normal((1, nq, dec.n_q_heads, dec.head_dim), dtype=np.float32)))
+        ov = torch.empty((1, nq, dec.n_q_heads, dec.head_dim), dtype=torch.float32, device=dev)
+        wsv = torch.empty(lib.attn_verify_workspace_bytes(1, nq, ctx, dec.n_q_heads),
+                          dtype=torch.uint8, device=dev)
+        us = group_us(lambda c: lib.attn_verify(qv, c, table, ctx_t, ctx, out=ov, workspace=wsv))
+        verify[f"nq{nq}"] = {"us": round(us, 3), "hbm_GBps": round(dec_b / (us * 1e-6) / 1e9, 1)}
+    part = lib.attn_decode_partition_rows(1, ctx, dec.n_kv_heads)
+    ws8 = torch.empty(lib.attn_decode_int8p_workspace_bytes(1, 1, ctx, dec.n_q_heads, dec.n_kv_heads),
+                      dtype=torch.uint8, device=dev)
+    i8p_us = group_us(lambda c: lib.attn_decode_int8p(q_dec, c, table, ctx_t, ctx, out=out_dec,
+                                                      workspace=ws8))
+    res["verify_ctx32768"] = verify
+    res["decode_int8p_ctx32768"] = {"us": round(i8p_us, 3), "partition": part,
+                                    "hbm_GBps": round(dec_b / (i8p_us * 1e-6) / 1e9, 1)}
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

@@ -297,6 +297,9 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
 // partitions costs one memory round trip. Query row z is query i = z % nq of sequence
 // s = z / nq and sees ctx - nq + i + 1 keys (nq = 1: one row per sequence).
 // out = sum_j o_j 2^(m_j - M) / sum_j l_j 2^(m_j - M), M = max_j m_j.
+// KIND only names the instantiation (0: after the one-row split kernel, 1: after the
+// int8 matrix-core split kernel) so that profiles tell the two apart.
+template <int KIND>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     const float* __restrict__ ws_m, const float* __restrict__ ws_l, const float* __restrict__ ws_o,
     const int32_t* __restrict__ ctx_lens, int ctx_cap, int n_q_heads, int max_parts, int nq,
@@ -374,7 +377,7 @@ int launch_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cach
                      ws_l, ws_o, max_parts, max_parts == 1 ? out : nullptr);
   int rc = check_launch("attn_decode stage 1");
   if (rc || max_parts == 1) return rc;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(kHeadDim / 64, n_q_heads, num_seqs), dim3(64), 0,
+  hipLaunchKernelGGL(decode_merge_kernel<0>, dim3(kHeadDim / 64, n_q_heads, num_seqs), dim3(64), 0,
                      stream, ws_m, ws_l, ws_o, ctx_lens, ctx_cap, n_q_heads, max_parts, 1, kPart, out);
   return check_launch("attn_decode stage 2");
 }
@@ -398,7 +401,7 @@ int launch_verify(const uint16_t* q, int nq, const int8_t* k_cache, const int8_t
 int launch_merge(const float* ws_m, const float* ws_l, const float* ws_o, const int32_t* ctx_lens,
                  int ctx_cap, int num_seqs, int nq, int n_q_heads, int max_parts, int part_rows,
                  float* out, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(kHeadDim / 64, n_q_heads, num_seqs * nq), dim3(64),
+  hipLaunchKernelGGL(decode_merge_kernel<1>, dim3(kHeadDim / 64, n_q_heads, num_seqs * nq), dim3(64),
                      0, stream, ws_m, ws_l, ws_o, ctx_lens, ctx_cap, n_q_heads, max_parts, nq,
                      part_rows, out);
   return check_launch("decode merge");
