@@ -21,14 +21,19 @@ Modules:
   quant      -- per-row absmax/127 int8 quantizer, bf16 widening.
   paged      -- the paged cache byte layout (write and gather), by index formula.
   attention  -- exact softmax attention, split-K partials + log-sum-exp merge,
-                int8-P emulation (per 64-key block) and a pure-Python brute force.
+                int8-P emulation (per 64-key block), multi-row verify forms and a
+                pure-Python brute force.
+  rope       -- rotary embedding from a caller cos/sin table (fp32 pairwise rule) and
+                the fused producer: rotate Q/K, quantize Q/K/V, paged K/V write.
 
 Pins (tests/test_oracle_*.py) tie every function to something other than itself:
 hand-derived tie cases, an fp64-then-round re-evaluation of the quantizer, the
 2080 B/token byte accounting, brute force on tiny inputs, closed forms (ctx=1,
 Q=0, equal keys, dominant key), softmax normalisation, merge = unsplit, page
-permutation invariance, and chunk row = decode at the matching context.
+permutation invariance, chunk row = decode at the matching context, verify rows =
+decode at each row's context; RoPE against complex multiplication, exact quarter
+turns, relative-position invariance of scores.
 The int8-P emulation is pinned by brute force, an exact special case and its
 error bound; beyond that its agreement with the pages is "parity unpinned".
 """
-from . import quant, paged, attention  # noqa: F401
+from . import quant, paged, attention, rope  # noqa: F401

@@ -221,6 +221,67 @@ def make_prefill_case(seed: int, ctx: int, n_new: int, *, pages: str = "random",
                        n_kv_heads=n_kv_heads, head_dim=head_dim)
 
 
+def rope_table(max_pos: int, rotary_dim: int, theta: float = 10000.0) -> np.ndarray:
+    """A caller's RoPE table cos_sin [max_pos, rotary_dim] fp32: for position p and pair
+    i < rotary_dim/2, cos and sin of p * theta^(-2i/rotary_dim) (evaluated in float64,
+    rounded to fp32), cos in the first half of the row, sin in the second."""
+    half = rotary_dim // 2
+    inv = theta ** (-np.arange(half, dtype=np.float64) * 2.0 / rotary_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+@dataclasses.dataclass
+class ProducerCase:
+    """One producer batch: T tokens of q/k/v rows, their positions and cache slots."""
+    seed: int
+    positions: np.ndarray    # int32 [T]
+    slots: np.ndarray        # int32 [T] (negative: skipped)
+    num_pages: int
+    rotary_dim: int
+    max_pos: int
+    n_q_heads: int = N_Q_HEADS
+    n_kv_heads: int = N_KV_HEADS
+    head_dim: int = HEAD_DIM
+
+    def data(self):
+        """(q [T,Hq,D], k [T,Hkv,D], v [T,Hkv,D]) fp32 N(0,1), K with 4 outlier channels x10."""
+        rng = np.random.default_rng([self.seed, 2000])
+        T = self.positions.shape[0]
+        q = rng.standard_normal((T, self.n_q_heads, self.head_dim), dtype=np.float32)
+        k = rng.standard_normal((T, self.n_kv_heads, self.head_dim), dtype=np.float32)
+        v = rng.standard_normal((T, self.n_kv_heads, self.head_dim), dtype=np.float32)
+        outl = rng.choice(self.head_dim, size=4, replace=False)
+        k[:, :, outl] *= np.float32(10.0)
+        return q, k, v
+
+    def table(self):
+        return rope_table(self.max_pos, self.rotary_dim)
+
+
+def make_producer_case(seed: int, n_tokens: int, *, start: int = 0, layout: str = "chunk",
+                       rotary_dim: int = HEAD_DIM, extra_pages: int = 2) -> ProducerCase:
+    """layout="chunk": tokens start..start+T-1 of one sequence at consecutive positions,
+    written to a random permutation of pages (whole-page runs where the chunk covers a
+    page); layout="scatter": T decode tokens of T sequences at random positions and random
+    slots (one slot per token, some slots skipped with -1)."""
+    rng = np.random.default_rng([seed, 2001])
+    if layout == "chunk":
+        pos = np.arange(start, start + n_tokens, dtype=np.int64)
+        n_pages = int(pos[-1] // PAGE) + 1 + extra_pages
+        perm = rng.permutation(n_pages)
+        slots = perm[pos // PAGE] * PAGE + pos % PAGE
+        max_pos = int(pos[-1]) + 1
+    else:
+        n_pages = n_tokens + extra_pages
+        pos = rng.integers(0, 131072, size=n_tokens)
+        slots = rng.permutation(n_pages * PAGE)[:n_tokens]
+        slots[rng.random(n_tokens) < 0.1] = -1
+        max_pos = 131072
+    return ProducerCase(seed=seed, positions=pos.astype(np.int32), slots=slots.astype(np.int32),
+                        num_pages=n_pages, rotary_dim=rotary_dim, max_pos=max_pos)
+
+
 def near_tie_rows(seed: int, n_rows: int, head_dim: int = HEAD_DIM) -> np.ndarray:
     """fp32 rows built to sit on or next to rounding ties of x/scale.
 
