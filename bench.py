@@ -293,6 +293,50 @@ def main():
                       dtype=torch.uint8, device=dev)
     i8p_us = group_us(lambda c: lib.attn_decode_int8p(q_dec, c, table, ctx_t, ctx, out=out_dec,
                                                       workspace=ws8))
+    # the fused producer (RoPE on Q/K, Q/K/V quantized, K/V paged write) for the chunk's
+    # 2,048 tokens and for one decode token, bf16 inputs as a projection would give them
+    qb = q_pf                                            # bf16 [2048, 24, 256]
+    kb = bf16(workloads.f32_to_bf16_bits(k4[pos0:]))
+    vb = bf16(workloads.f32_to_bf16_bits(v4[pos0:]))
+    pos_t = torch.arange(pos0, pf.context_len, dtype=torch.int32, device=dev)
+    rope_tab = up(workloads.rope_table(pf.context_len, pf.head_dim))
+    prod_bytes = pf.n_new * (2 * pf.head_dim * (pf.n_q_heads + 2 * pf.n_kv_heads)
+                             + pf.head_dim * (pf.n_q_heads + 2 * pf.n_kv_heads)
+                             + 4 * (pf.n_q_heads + 2 * pf.n_kv_heads) + 8)
+    for _ in range(3):
+        lib.kv_produce(qb, kb, vb, pos_t, rope_tab, s_chunk, pcache)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        lib.kv_produce(qb, kb, vb, pos_t, rope_tab, s_chunk, pcache)
+    e1.record()
+    torch.cuda.synchronize()
+    prod_us = e0.elapsed_time(e1) * 1e3 / 20
+    # one decode token: the eager Python call costs more host time than the kernel takes,
+    # so 8 calls are captured once in a graph and the graph is replayed
+    one = (qb[-1:], kb[-1:], vb[-1:], pos_t[-1:], rope_tab, s_chunk[-1:], pcache)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lib.kv_produce(*one)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(8):
+            lib.kv_produce(*one)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(20):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    tok1 = e0.elapsed_time(e1) * 1e3 / 160
+    res["produce_2048"] = {"us": round(prod_us, 3), "bytes": prod_bytes,
+                           "hbm_GBps": round(prod_bytes / (prod_us * 1e-6) / 1e9, 1),
+                           "one_token_us_graph": round(tok1, 3)}
     res["verify_ctx32768"] = verify
     res["decode_int8p_ctx32768"] = {"us": round(i8p_us, 3), "partition": part,
                                     "hbm_GBps": round(dec_b / (i8p_us * 1e-6) / 1e9, 1)}

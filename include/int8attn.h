@@ -104,6 +104,38 @@ int kv_quant_write(const void* k, const void* v, int in_dtype,
                    float* k_scale, float* v_scale,
                    int num_pages, void* stream);
 
+/* kv_produce -- the fused producer: RoPE on the new Q and K rows, then Q, K and V
+ * quantized with the kv_quant_write rule, K/V codes and scales written into the paged
+ * cache and Q kept as int8 codes + scales, in one launch.
+ * [DCU §2.2: read Q/K/V, apply RoPE to Q/K, reduce each row's absmax, compute the scale
+ *  and quantize, write the K/V codes and scales into the paged cache, and skip writing
+ *  back high-precision Q/K; the query is quantized once and reused by every partition.]
+ *
+ *  q             [n_tokens][n_q_heads][head_dim] (fp32 or bf16 as in_dtype), or NULL
+ *                together with q_codes and q_scales (K/V only).
+ *  k, v, slot_mapping, caches, num_pages: as for kv_quant_write.
+ *  positions     int32 [n_tokens]: the position of each token (the RoPE angle index);
+ *                values outside [0, max_position) are clamped into it (memory-safe,
+ *                result unspecified).
+ *  cos_sin       fp32 [max_position][rotary_dim], 16-byte aligned: row p holds the cos of
+ *                pairs 0..rotary_dim/2-1, then their sin. The frequencies, base and any
+ *                scaling of the caller's RoPE live in this table.
+ *  rotary_dim    0 (no rotation) or a multiple of 8 up to head_dim: pair (i, i +
+ *                rotary_dim/2), i < rotary_dim/2, of each Q and K row turns by row p of
+ *                the table; dims >= rotary_dim pass through. In fp32 with every product
+ *                and sum rounded on its own: x_i' = x_i c - x_j s, x_j' = x_j c + x_i s.
+ *  q_codes       int8 [n_tokens][n_q_heads][head_dim] and q_scales fp32
+ *                [n_tokens][n_q_heads]: the rotated Q rows quantized (the *_q8 attention
+ *                entry points take them as they are).
+ *  V rows are not rotated. Codes and scales are bit-exact functions of the inputs and
+ *  the table. */
+int kv_produce(const void* q, const void* k, const void* v, int in_dtype,
+               int n_tokens, int n_q_heads, int n_kv_heads, int head_dim,
+               const int32_t* positions, const float* cos_sin, int rotary_dim,
+               int max_position, const int32_t* slot_mapping,
+               int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale,
+               int num_pages, int8_t* q_codes, float* q_scales, void* stream);
+
 /* q_quant -- quantize bf16 query rows with the same rule [DCU §2.2: the query is
  * quantized once per token and head]. The attention entry points do this internally
  * with the same device routine; this entry exposes it for inspection.
@@ -260,6 +292,43 @@ int attn_prefill_chunk(const uint16_t* q, int n_new,
                        const int32_t* block_table, int context_len, int causal,
                        int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
                        float sm_scale, float* out, void* stream);
+
+/* *_q8 forms: the same computations with the query given as int8 codes and fp32 scales
+ * (the format kv_produce writes: q_codes [rows][head_dim], q_scales [rows], rows laid
+ * out as the bf16 q of the plain form) instead of bf16 rows that the call quantizes.
+ * [DCU §2.2: the query is quantized once by the producer and reused by every
+ *  partition.] Given q_codes/q_scales = q_quant(q), each returns bit for bit what the
+ * plain form returns for q. q_scales NULL with work to do returns I8A_EINVAL. */
+int attn_decode_q8(const int8_t* q_codes, const float* q_scales,
+                   const int8_t* k_cache, const int8_t* v_cache,
+                   const float* k_scale, const float* v_scale,
+                   const int32_t* block_table, int max_blocks_per_seq,
+                   const int32_t* context_lens, int num_seqs, int max_context_len,
+                   int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                   float sm_scale, float* out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+int attn_verify_q8(const int8_t* q_codes, const float* q_scales, int nq,
+                   const int8_t* k_cache, const int8_t* v_cache,
+                   const float* k_scale, const float* v_scale,
+                   const int32_t* block_table, int max_blocks_per_seq,
+                   const int32_t* context_lens, int num_seqs, int max_context_len,
+                   int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                   float sm_scale, float* out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+int attn_decode_int8p_q8(const int8_t* q_codes, const float* q_scales, int nq,
+                         const int8_t* k_cache, const int8_t* v_cache,
+                         const float* k_scale, const float* v_scale,
+                         const int32_t* block_table, int max_blocks_per_seq,
+                         const int32_t* context_lens, int num_seqs, int max_context_len,
+                         int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                         int partition_rows, float sm_scale, float* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+int attn_prefill_chunk_q8(const int8_t* q_codes, const float* q_scales, int n_new,
+                          const int8_t* k_cache, const int8_t* v_cache,
+                          const float* k_scale, const float* v_scale,
+                          const int32_t* block_table, int context_len, int causal,
+                          int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                          float sm_scale, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,14 +18,16 @@ import torch
 __all__ = ["lib", "PagedCache", "alloc_cache", "kv_quant_write", "q_quant", "attn_decode",
            "attn_decode_workspace_bytes", "attn_verify", "attn_verify_workspace_bytes",
            "attn_decode_int8p", "attn_decode_int8p_workspace_bytes", "attn_decode_partition_rows",
-           "attn_prefill_chunk", "Int8AttnError",
+           "attn_prefill_chunk", "kv_produce", "Int8AttnError",
            "HEAD_DIM", "PAGE", "PARTITION", "EXPORTED_SYMBOLS"]
 
 HEAD_DIM = 256
 PAGE = 16
 PARTITION = 512
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint8attn.so")
-EXPORTED_SYMBOLS = ("int8attn_last_error", "int8attn_version", "kv_quant_write", "q_quant",
+EXPORTED_SYMBOLS = ("int8attn_last_error", "int8attn_version", "kv_quant_write", "kv_produce",
+                    "q_quant", "attn_decode_q8", "attn_verify_q8", "attn_decode_int8p_q8",
+                    "attn_prefill_chunk_q8",
                     "attn_decode_workspace_bytes", "attn_decode", "attn_verify_workspace_bytes",
                     "attn_verify", "attn_decode_partition_rows",
                     "attn_decode_int8p_workspace_bytes", "attn_decode_int8p",
@@ -41,7 +43,23 @@ _SIGNATURES = {
     "int8attn_version": (_c_int, []),
     "kv_quant_write": (_c_int, [_c_void, _c_void, _c_int, _c_int, _c_int, _c_int, _c_void,
                                 _c_void, _c_void, _c_void, _c_void, _c_int, _c_void]),
+    "kv_produce": (_c_int, [_c_void, _c_void, _c_void, _c_int, _c_int, _c_int, _c_int, _c_int,
+                            _c_void, _c_void, _c_int, _c_int, _c_void, _c_void, _c_void, _c_void,
+                            _c_void, _c_int, _c_void, _c_void, _c_void]),
     "q_quant": (_c_int, [_c_void, _c_int, _c_int, _c_void, _c_void, _c_void]),
+    "attn_decode_q8": (_c_int, [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void, _c_void,
+                                _c_int, _c_void, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                _c_float, _c_void, _c_void, _c_size, _c_void]),
+    "attn_verify_q8": (_c_int, [_c_void, _c_void, _c_int, _c_void, _c_void, _c_void, _c_void,
+                                _c_void, _c_int, _c_void, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                _c_int, _c_float, _c_void, _c_void, _c_size, _c_void]),
+    "attn_decode_int8p_q8": (_c_int, [_c_void, _c_void, _c_int, _c_void, _c_void, _c_void,
+                                      _c_void, _c_void, _c_int, _c_void, _c_int, _c_int, _c_int,
+                                      _c_int, _c_int, _c_int, _c_int, _c_float, _c_void, _c_void,
+                                      _c_size, _c_void]),
+    "attn_prefill_chunk_q8": (_c_int, [_c_void, _c_void, _c_int, _c_void, _c_void, _c_void,
+                                       _c_void, _c_void, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_int, _c_float, _c_void, _c_void]),
     "attn_decode_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "attn_decode": (_c_int, [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void, _c_int,
                              _c_void, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
@@ -159,6 +177,56 @@ def kv_quant_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                                 cache.num_pages, _stream(stream)))
 
 
+def kv_produce(q, k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
+               cos_sin: torch.Tensor | None, slot_mapping: torch.Tensor, cache,
+               rotary_dim: int | None = None, stream=None):
+    """Fused producer: RoPE on q [T, Hq, 256] and k [T, Hkv, 256] (fp32 or bf16, one dtype)
+    from the table cos_sin [max_pos, rotary_dim] (cos half, then sin half), quantize q, k,
+    v, write k/v into the paged cache at their slots. Returns (q_codes int8 [T, Hq, 256],
+    q_scales fp32 [T, Hq]), or None when q is None. rotary_dim defaults to the table width
+    (0: no rotation)."""
+    if k.dim() != 3 or k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("k and v must both be [T, Hkv, head_dim] of one dtype")
+    T, H, D = k.shape
+    dt = {torch.float32: 0, torch.bfloat16: 1}.get(k.dtype)
+    if dt is None:
+        raise TypeError("k/v must be float32 or bfloat16")
+    if slot_mapping.shape != (T,) or positions.shape != (T,):
+        raise ValueError("slot_mapping and positions must be [T]")
+    if H != cache.n_kv_heads:
+        raise ValueError("k/v head count differs from the cache")
+    rd = (cos_sin.shape[1] if cos_sin is not None else 0) if rotary_dim is None else int(rotary_dim)
+    max_pos = cos_sin.shape[0] if cos_sin is not None else 0
+    cs = _dev(cos_sin, "cos_sin", torch.float32) if cos_sin is not None else None
+    if q is not None:
+        if q.dim() != 3 or q.shape[0] != T or q.shape[2] != D or q.dtype != k.dtype:
+            raise ValueError("q must be [T, Hq, head_dim] of k's dtype")
+        Hq = q.shape[1]
+        codes = torch.empty(q.shape, dtype=torch.int8, device=k.device)
+        scales = torch.empty(q.shape[:2], dtype=torch.float32, device=k.device)
+        qp, cp, sp = _dev(q, "q"), codes.data_ptr(), scales.data_ptr()
+    else:
+        Hq, qp, cp, sp = 6 * H, None, None, None
+    _check(lib().kv_produce(qp, _dev(k, "k"), _dev(v, "v"), dt, T, Hq, H, D,
+                            _dev(positions, "positions", torch.int32), cs, rd, max_pos,
+                            _dev(slot_mapping, "slot_mapping", torch.int32), *cache.ptrs(),
+                            cache.num_pages, cp, sp, _stream(stream)))
+    return (codes, scales) if q is not None else None
+
+
+def _query(q: torch.Tensor, q_scales, dims: int, what: str):
+    """bf16 rows (q_scales None) or int8 codes + fp32 scales of the same leading shape."""
+    if q.dim() != dims:
+        raise TypeError(f"q must have {dims} dims ({what})")
+    if q_scales is None:
+        if q.dtype != torch.bfloat16:
+            raise TypeError("q must be bfloat16, or int8 codes with q_scales")
+        return None
+    if q.dtype != torch.int8 or q_scales.dtype != torch.float32 or q_scales.shape != q.shape[:-1]:
+        raise TypeError("int8 q needs fp32 q_scales of shape q.shape[:-1]")
+    return _dev(q_scales, "q_scales", torch.float32)
+
+
 def q_quant(q: torch.Tensor, stream=None):
     """bf16 rows [..., 256] -> (int8 codes [..., 256], fp32 scales [...])."""
     if q.dtype != torch.bfloat16:
@@ -179,10 +247,11 @@ def attn_decode_workspace_bytes(num_seqs: int, max_context_len: int, n_q_heads: 
 
 def attn_decode(q: torch.Tensor, cache, block_table: torch.Tensor, context_lens: torch.Tensor,
                 max_context_len: int, sm_scale: float | None = None, out: torch.Tensor | None = None,
-                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Decode: q bf16 [S, Hq, 256] -> out fp32 [S, Hq, 256] over the paged INT8 cache."""
-    if q.dtype != torch.bfloat16 or q.dim() != 3:
-        raise TypeError("q must be bfloat16 [S, Hq, head_dim]")
+                workspace: torch.Tensor | None = None, stream=None,
+                q_scales: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode: q bf16 [S, Hq, 256] (or int8 codes with q_scales [S, Hq]) -> out fp32
+    [S, Hq, 256] over the paged INT8 cache."""
+    qs = _query(q, q_scales, 3, "[S, Hq, head_dim]")
     S, Hq, D = q.shape
     if block_table.dim() != 2 or block_table.shape[0] != S:
         raise ValueError("block_table must be [S, max_blocks]")
@@ -194,7 +263,9 @@ def attn_decode(q: torch.Tensor, cache, block_table: torch.Tensor, context_lens:
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     sm = float(sm_scale if sm_scale is not None else D ** -0.5)
-    _check(lib().attn_decode(_dev(q, "q"), *cache.ptrs(),
+    fn, head = ((lib().attn_decode, (_dev(q, "q"),)) if qs is None
+                else (lib().attn_decode_q8, (_dev(q, "q"), qs)))
+    _check(fn(*head, *cache.ptrs(),
                              _dev(block_table, "block_table", torch.int32), block_table.shape[1],
                              _dev(context_lens, "context_lens", torch.int32), S,
                              int(max_context_len), cache.num_pages, Hq, cache.n_kv_heads, D, sm,
@@ -210,11 +281,11 @@ def attn_verify_workspace_bytes(num_seqs: int, nq: int, max_context_len: int, n_
 
 def attn_verify(q: torch.Tensor, cache, block_table: torch.Tensor, context_lens: torch.Tensor,
                 max_context_len: int, sm_scale: float | None = None, out: torch.Tensor | None = None,
-                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Multi-row decode: q bf16 [S, nq, Hq, 256] (query i of a sequence at position
-    ctx - nq + i) -> out fp32 [S, nq, Hq, 256] over the paged INT8 cache."""
-    if q.dtype != torch.bfloat16 or q.dim() != 4:
-        raise TypeError("q must be bfloat16 [S, nq, Hq, head_dim]")
+                workspace: torch.Tensor | None = None, stream=None,
+                q_scales: torch.Tensor | None = None) -> torch.Tensor:
+    """Multi-row decode: q bf16 [S, nq, Hq, 256] (or int8 codes with q_scales [S, nq, Hq];
+    query i of a sequence at position ctx - nq + i) -> out fp32 [S, nq, Hq, 256]."""
+    qs = _query(q, q_scales, 4, "[S, nq, Hq, head_dim]")
     S, nq, Hq, D = q.shape
     if block_table.dim() != 2 or block_table.shape[0] != S:
         raise ValueError("block_table must be [S, max_blocks]")
@@ -226,7 +297,9 @@ def attn_verify(q: torch.Tensor, cache, block_table: torch.Tensor, context_lens:
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     sm = float(sm_scale if sm_scale is not None else D ** -0.5)
-    _check(lib().attn_verify(_dev(q, "q"), nq, *cache.ptrs(),
+    fn, head = ((lib().attn_verify, (_dev(q, "q"),)) if qs is None
+                else (lib().attn_verify_q8, (_dev(q, "q"), qs)))
+    _check(fn(*head, nq, *cache.ptrs(),
                              _dev(block_table, "block_table", torch.int32), block_table.shape[1],
                              _dev(context_lens, "context_lens", torch.int32), S,
                              int(max_context_len), cache.num_pages, Hq, cache.n_kv_heads, D, sm,
@@ -249,11 +322,11 @@ def attn_decode_int8p_workspace_bytes(num_seqs: int, nq: int, max_context_len: i
 def attn_decode_int8p(q: torch.Tensor, cache, block_table: torch.Tensor,
                       context_lens: torch.Tensor, max_context_len: int, partition_rows: int = 0,
                       sm_scale: float | None = None, out: torch.Tensor | None = None,
-                      workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Int8-P decode/verify: q bf16 [S, Hq, 256] (one row) or [S, nq, Hq, 256] -> out fp32
-    of the same shape."""
-    if q.dtype != torch.bfloat16 or q.dim() not in (3, 4):
-        raise TypeError("q must be bfloat16 [S, Hq, head_dim] or [S, nq, Hq, head_dim]")
+                      workspace: torch.Tensor | None = None, stream=None,
+                      q_scales: torch.Tensor | None = None) -> torch.Tensor:
+    """Int8-P decode/verify: q bf16 [S, Hq, 256] (one row) or [S, nq, Hq, 256] (or int8
+    codes with q_scales) -> out fp32 of the same shape."""
+    qs = _query(q, q_scales, q.dim() if q.dim() in (3, 4) else 4, "[S, (nq,) Hq, head_dim]")
     one_row = q.dim() == 3
     q4 = q.unsqueeze(1) if one_row else q
     S, nq, Hq, D = q4.shape
@@ -268,7 +341,9 @@ def attn_decode_int8p(q: torch.Tensor, cache, block_table: torch.Tensor,
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     sm = float(sm_scale if sm_scale is not None else D ** -0.5)
-    _check(lib().attn_decode_int8p(_dev(q4, "q"), nq, *cache.ptrs(),
+    fn, head = ((lib().attn_decode_int8p, (_dev(q4, "q"),)) if qs is None
+                else (lib().attn_decode_int8p_q8, (_dev(q4, "q"), qs)))
+    _check(fn(*head, nq, *cache.ptrs(),
                                    _dev(block_table, "block_table", torch.int32),
                                    block_table.shape[1],
                                    _dev(context_lens, "context_lens", torch.int32), S,
@@ -281,17 +356,20 @@ def attn_decode_int8p(q: torch.Tensor, cache, block_table: torch.Tensor,
 
 def attn_prefill_chunk(q: torch.Tensor, cache, block_table: torch.Tensor, context_len: int,
                        causal: bool = True, sm_scale: float | None = None,
-                       out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Chunk: q bf16 [n_new, Hq, 256] at the tail of one sequence -> out fp32 [n_new, Hq, 256]."""
-    if q.dtype != torch.bfloat16 or q.dim() != 3:
-        raise TypeError("q must be bfloat16 [n_new, Hq, head_dim]")
+                       out: torch.Tensor | None = None, stream=None,
+                       q_scales: torch.Tensor | None = None) -> torch.Tensor:
+    """Chunk: q bf16 [n_new, Hq, 256] (or int8 codes with q_scales [n_new, Hq]) at the
+    tail of one sequence -> out fp32 [n_new, Hq, 256]."""
+    qs = _query(q, q_scales, 3, "[n_new, Hq, head_dim]")
     n_new, Hq, D = q.shape
     if block_table.dim() != 1 or block_table.numel() < (context_len + PAGE - 1) // PAGE:
         raise ValueError("block_table must be [ceil(context_len/16)]")
     if out is None:
         out = torch.empty((n_new, Hq, D), dtype=torch.float32, device=q.device)
     sm = float(sm_scale if sm_scale is not None else D ** -0.5)
-    _check(lib().attn_prefill_chunk(_dev(q, "q"), n_new, *cache.ptrs(),
+    fn, head = ((lib().attn_prefill_chunk, (_dev(q, "q"),)) if qs is None
+                else (lib().attn_prefill_chunk_q8, (_dev(q, "q"), qs)))
+    _check(fn(*head, n_new, *cache.ptrs(),
                                     _dev(block_table, "block_table", torch.int32),
                                     int(context_len), int(bool(causal)), cache.num_pages, Hq,
                                     cache.n_kv_heads, D, sm,

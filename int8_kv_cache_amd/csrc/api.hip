@@ -98,6 +98,34 @@ int kv_quant_write(const void* k, const void* v, int in_dtype, int n_tokens, int
                                (hipStream_t)stream);
 }
 
+int kv_produce(const void* q, const void* k, const void* v, int in_dtype, int n_tokens,
+               int n_q_heads, int n_kv_heads, int head_dim, const int32_t* positions,
+               const float* cos_sin, int rotary_dim, int max_position,
+               const int32_t* slot_mapping, int8_t* k_cache, int8_t* v_cache, float* k_scale,
+               float* v_scale, int num_pages, int8_t* q_codes, float* q_scales, void* stream) {
+  if (in_dtype != I8A_DTYPE_F32 && in_dtype != I8A_DTYPE_BF16)
+    return set_error(I8A_EINVAL, "kv_produce: in_dtype %d", in_dtype);
+  int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
+  if (rc) return rc;
+  if (n_tokens < 0 || num_pages <= 0 || (long long)n_tokens * n_q_heads > 2147483000LL)
+    return set_error(I8A_EINVAL, "kv_produce: n_tokens %d, num_pages %d", n_tokens, num_pages);
+  if (rotary_dim < 0 || rotary_dim > head_dim || rotary_dim % 8 != 0)
+    return set_error(I8A_EINVAL, "kv_produce: rotary_dim %d (0..256, a multiple of 8)", rotary_dim);
+  if (rotary_dim > 0 && (max_position <= 0 || !cos_sin || !positions))
+    return set_error(I8A_EINVAL, "kv_produce: RoPE needs positions, cos_sin and max_position > 0");
+  if ((q_codes == nullptr) != (q_scales == nullptr) || (q_codes != nullptr && q == nullptr))
+    return set_error(I8A_EINVAL, "kv_produce: q, q_codes and q_scales go together");
+  if (n_tokens == 0) return I8A_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
+    return set_error(I8A_EINVAL, "kv_produce: null pointer");
+  if (rotary_dim > 0 && ((uintptr_t)cos_sin & 15u) != 0)
+    return set_error(I8A_EINVAL, "kv_produce: cos_sin not 16-byte aligned");
+  return launch_kv_produce(q, k, v, in_dtype == I8A_DTYPE_BF16, n_tokens, n_q_heads, n_kv_heads,
+                           positions, cos_sin, rotary_dim, max_position > 0 ? max_position : 1,
+                           slot_mapping, k_cache, v_cache, k_scale, v_scale, num_pages, q_codes,
+                           q_scales, (hipStream_t)stream);
+}
+
 int q_quant(const uint16_t* q_bf16, int n_rows, int head_dim, int8_t* codes, float* scales,
             void* stream) {
   if (n_rows < 0 || n_rows > 2147483000) return set_error(I8A_EINVAL, "q_quant: n_rows %d", n_rows);
@@ -112,12 +140,15 @@ size_t attn_decode_workspace_bytes(int num_seqs, int max_context_len, int n_q_he
   return decode_ws_bytes(num_seqs, max_context_len, n_q_heads);
 }
 
-int attn_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cache,
-                const float* k_scale, const float* v_scale, const int32_t* block_table,
-                int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
-                int max_context_len, int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
-                float sm_scale, float* out, void* workspace, size_t workspace_bytes,
-                void* stream) {
+// The attention entry points take the query either as bf16 rows (quantized inside) or,
+// in their *_q8 forms, as int8 codes with fp32 scales (kv_produce's output): q_scales
+// is null for the former.
+static int decode_impl(const void* q, const float* q_scales, const int8_t* k_cache,
+                       const int8_t* v_cache, const float* k_scale, const float* v_scale,
+                       const int32_t* block_table, int max_blocks_per_seq,
+                       const int32_t* context_lens, int num_seqs, int max_context_len,
+                       int num_pages, int n_q_heads, int n_kv_heads, int head_dim, float sm_scale,
+                       float* out, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
   if (rc) return rc;
   if (num_seqs < 0 || num_seqs > 65535) return set_error(I8A_EINVAL, "attn_decode: num_seqs %d", num_seqs);
@@ -134,9 +165,35 @@ int attn_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cache,
   if (workspace_bytes < need)
     return set_error(I8A_EWORKSPACE, "attn_decode: workspace %zu bytes < %zu needed", workspace_bytes, need);
   const int max_parts = (max_context_len + 511) / 512;
-  return launch_decode(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks_per_seq,
-                       context_lens, num_seqs, max_context_len, num_pages, n_q_heads, n_kv_heads,
-                       sm_scale, out, (float*)workspace, max_parts, (hipStream_t)stream);
+  return launch_decode(q, q_scales, k_cache, v_cache, k_scale, v_scale, block_table,
+                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_pages,
+                       n_q_heads, n_kv_heads, sm_scale, out, (float*)workspace, max_parts,
+                       (hipStream_t)stream);
+}
+
+int attn_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cache,
+                const float* k_scale, const float* v_scale, const int32_t* block_table,
+                int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                int max_context_len, int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  return decode_impl(q, nullptr, k_cache, v_cache, k_scale, v_scale, block_table,
+                     max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_pages,
+                     n_q_heads, n_kv_heads, head_dim, sm_scale, out, workspace, workspace_bytes,
+                     stream);
+}
+
+int attn_decode_q8(const int8_t* q_codes, const float* q_scales, const int8_t* k_cache,
+                   const int8_t* v_cache, const float* k_scale, const float* v_scale,
+                   const int32_t* block_table, int max_blocks_per_seq,
+                   const int32_t* context_lens, int num_seqs, int max_context_len, int num_pages,
+                   int n_q_heads, int n_kv_heads, int head_dim, float sm_scale, float* out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q_scales && num_seqs > 0) return set_error(I8A_EINVAL, "attn_decode_q8: null q_scales");
+  return decode_impl(q_codes, q_scales, k_cache, v_cache, k_scale, v_scale, block_table,
+                     max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_pages,
+                     n_q_heads, n_kv_heads, head_dim, sm_scale, out, workspace, workspace_bytes,
+                     stream);
 }
 
 size_t attn_verify_workspace_bytes(int num_seqs, int nq, int max_context_len, int n_q_heads,
@@ -146,12 +203,12 @@ size_t attn_verify_workspace_bytes(int num_seqs, int nq, int max_context_len, in
   return decode_ws_bytes((long long)num_seqs * nq, max_context_len, n_q_heads);
 }
 
-int attn_verify(const uint16_t* q, int nq, const int8_t* k_cache, const int8_t* v_cache,
-                const float* k_scale, const float* v_scale, const int32_t* block_table,
-                int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
-                int max_context_len, int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
-                float sm_scale, float* out, void* workspace, size_t workspace_bytes,
-                void* stream) {
+static int verify_impl(const void* q, const float* q_scales, int nq, const int8_t* k_cache,
+                       const int8_t* v_cache, const float* k_scale, const float* v_scale,
+                       const int32_t* block_table, int max_blocks_per_seq,
+                       const int32_t* context_lens, int num_seqs, int max_context_len,
+                       int num_pages, int n_q_heads, int n_kv_heads, int head_dim, float sm_scale,
+                       float* out, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
   if (rc) return rc;
   if (nq < 1 || nq > 8) return set_error(I8A_EINVAL, "attn_verify: nq %d outside 1..8", nq);
@@ -170,9 +227,35 @@ int attn_verify(const uint16_t* q, int nq, const int8_t* k_cache, const int8_t* 
   if (workspace_bytes < need)
     return set_error(I8A_EWORKSPACE, "attn_verify: workspace %zu bytes < %zu needed", workspace_bytes, need);
   const int max_parts = (max_context_len + 511) / 512;
-  return launch_verify(q, nq, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks_per_seq,
-                       context_lens, num_seqs, max_context_len, num_pages, n_q_heads, n_kv_heads,
-                       sm_scale, out, (float*)workspace, max_parts, (hipStream_t)stream);
+  return launch_verify(q, q_scales, nq, k_cache, v_cache, k_scale, v_scale, block_table,
+                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_pages,
+                       n_q_heads, n_kv_heads, sm_scale, out, (float*)workspace, max_parts,
+                       (hipStream_t)stream);
+}
+
+int attn_verify(const uint16_t* q, int nq, const int8_t* k_cache, const int8_t* v_cache,
+                const float* k_scale, const float* v_scale, const int32_t* block_table,
+                int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                int max_context_len, int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  return verify_impl(q, nullptr, nq, k_cache, v_cache, k_scale, v_scale, block_table,
+                     max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_pages,
+                     n_q_heads, n_kv_heads, head_dim, sm_scale, out, workspace, workspace_bytes,
+                     stream);
+}
+
+int attn_verify_q8(const int8_t* q_codes, const float* q_scales, int nq, const int8_t* k_cache,
+                   const int8_t* v_cache, const float* k_scale, const float* v_scale,
+                   const int32_t* block_table, int max_blocks_per_seq,
+                   const int32_t* context_lens, int num_seqs, int max_context_len, int num_pages,
+                   int n_q_heads, int n_kv_heads, int head_dim, float sm_scale, float* out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q_scales && num_seqs > 0) return set_error(I8A_EINVAL, "attn_verify_q8: null q_scales");
+  return verify_impl(q_codes, q_scales, nq, k_cache, v_cache, k_scale, v_scale, block_table,
+                     max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_pages,
+                     n_q_heads, n_kv_heads, head_dim, sm_scale, out, workspace, workspace_bytes,
+                     stream);
 }
 
 int attn_decode_partition_rows(int num_seqs, int max_context_len, int n_kv_heads) {
@@ -197,12 +280,13 @@ size_t attn_decode_int8p_workspace_bytes(int num_seqs, int nq, int max_context_l
   return partials_bytes((long long)num_seqs * nq, max_context_len, n_q_heads, part);
 }
 
-int attn_decode_int8p(const uint16_t* q, int nq, const int8_t* k_cache, const int8_t* v_cache,
-                      const float* k_scale, const float* v_scale, const int32_t* block_table,
-                      int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
-                      int max_context_len, int num_pages, int n_q_heads, int n_kv_heads,
-                      int head_dim, int partition_rows, float sm_scale, float* out,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+static int int8p_impl(const void* q, const float* q_scales, int nq, const int8_t* k_cache,
+                      const int8_t* v_cache, const float* k_scale, const float* v_scale,
+                      const int32_t* block_table, int max_blocks_per_seq,
+                      const int32_t* context_lens, int num_seqs, int max_context_len,
+                      int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                      int partition_rows, float sm_scale, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
   if (rc) return rc;
   if (nq < 1 || nq > 8) return set_error(I8A_EINVAL, "attn_decode_int8p: nq %d outside 1..8", nq);
@@ -226,16 +310,43 @@ int attn_decode_int8p(const uint16_t* q, int nq, const int8_t* k_cache, const in
   if (workspace_bytes < need)
     return set_error(I8A_EWORKSPACE, "attn_decode_int8p: workspace %zu bytes < %zu needed",
                      workspace_bytes, need);
-  return launch_decode_i8pv(1, part, q, nq, k_cache, v_cache, k_scale, v_scale, block_table,
-                            max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_pages,
-                            n_q_heads, n_kv_heads, sm_scale, out, (float*)workspace,
-                            (hipStream_t)stream);
+  return launch_decode_i8pv(1, part, q, q_scales, nq, k_cache, v_cache, k_scale, v_scale,
+                            block_table, max_blocks_per_seq, context_lens, num_seqs,
+                            max_context_len, num_pages, n_q_heads, n_kv_heads, sm_scale, out,
+                            (float*)workspace, (hipStream_t)stream);
 }
 
-int attn_prefill_chunk(const uint16_t* q, int n_new, const int8_t* k_cache, const int8_t* v_cache,
-                       const float* k_scale, const float* v_scale, const int32_t* block_table,
-                       int context_len, int causal, int num_pages, int n_q_heads, int n_kv_heads,
-                       int head_dim, float sm_scale, float* out, void* stream) {
+int attn_decode_int8p(const uint16_t* q, int nq, const int8_t* k_cache, const int8_t* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* block_table,
+                      int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                      int max_context_len, int num_pages, int n_q_heads, int n_kv_heads,
+                      int head_dim, int partition_rows, float sm_scale, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return int8p_impl(q, nullptr, nq, k_cache, v_cache, k_scale, v_scale, block_table,
+                    max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_pages,
+                    n_q_heads, n_kv_heads, head_dim, partition_rows, sm_scale, out, workspace,
+                    workspace_bytes, stream);
+}
+
+int attn_decode_int8p_q8(const int8_t* q_codes, const float* q_scales, int nq,
+                         const int8_t* k_cache, const int8_t* v_cache, const float* k_scale,
+                         const float* v_scale, const int32_t* block_table, int max_blocks_per_seq,
+                         const int32_t* context_lens, int num_seqs, int max_context_len,
+                         int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                         int partition_rows, float sm_scale, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!q_scales && num_seqs > 0) return set_error(I8A_EINVAL, "attn_decode_int8p_q8: null q_scales");
+  return int8p_impl(q_codes, q_scales, nq, k_cache, v_cache, k_scale, v_scale, block_table,
+                    max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_pages,
+                    n_q_heads, n_kv_heads, head_dim, partition_rows, sm_scale, out, workspace,
+                    workspace_bytes, stream);
+}
+
+static int prefill_impl(const void* q, const float* q_scales, int n_new, const int8_t* k_cache,
+                        const int8_t* v_cache, const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, int context_len, int causal, int num_pages,
+                        int n_q_heads, int n_kv_heads, int head_dim, float sm_scale, float* out,
+                        void* stream) {
   int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
   if (rc) return rc;
   if (n_new < 0 || context_len < 1 || n_new > context_len || num_pages <= 0 ||
@@ -250,9 +361,29 @@ int attn_prefill_chunk(const uint16_t* q, int n_new, const int8_t* k_cache, cons
   if (n_new == 0) return I8A_OK;
   if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_table || !out)
     return set_error(I8A_EINVAL, "attn_prefill_chunk: null pointer");
-  return launch_prefill(q, n_new, k_cache, v_cache, k_scale, v_scale, block_table, context_len,
-                        causal, num_pages, n_q_heads, n_kv_heads, sm_scale, out,
+  return launch_prefill(q, q_scales, n_new, k_cache, v_cache, k_scale, v_scale, block_table,
+                        context_len, causal, num_pages, n_q_heads, n_kv_heads, sm_scale, out,
                         (hipStream_t)stream);
+}
+
+int attn_prefill_chunk(const uint16_t* q, int n_new, const int8_t* k_cache, const int8_t* v_cache,
+                       const float* k_scale, const float* v_scale, const int32_t* block_table,
+                       int context_len, int causal, int num_pages, int n_q_heads, int n_kv_heads,
+                       int head_dim, float sm_scale, float* out, void* stream) {
+  return prefill_impl(q, nullptr, n_new, k_cache, v_cache, k_scale, v_scale, block_table,
+                      context_len, causal, num_pages, n_q_heads, n_kv_heads, head_dim, sm_scale,
+                      out, stream);
+}
+
+int attn_prefill_chunk_q8(const int8_t* q_codes, const float* q_scales, int n_new,
+                          const int8_t* k_cache, const int8_t* v_cache, const float* k_scale,
+                          const float* v_scale, const int32_t* block_table, int context_len,
+                          int causal, int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                          float sm_scale, float* out, void* stream) {
+  if (!q_scales && n_new > 0) return set_error(I8A_EINVAL, "attn_prefill_chunk_q8: null q_scales");
+  return prefill_impl(q_codes, q_scales, n_new, k_cache, v_cache, k_scale, v_scale, block_table,
+                      context_len, causal, num_pages, n_q_heads, n_kv_heads, head_dim, sm_scale,
+                      out, stream);
 }
 
 }  // extern "C"

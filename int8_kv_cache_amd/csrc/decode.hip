@@ -35,8 +35,12 @@ __device__ __forceinline__ float from_lane_plus6(float v) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x106, 0xF, 0xF, true));
 }
 
+// Q8: the query arrives as int8 codes [S][Hq][D] with fp32 scales [S][Hq] (kv_produce's
+// output) instead of bf16 rows to quantize.
+template <int Q8>
 __global__ __launch_bounds__(512, 1) void decode_split_kernel(
-    const uint16_t* __restrict__ q, const int8_t* __restrict__ k_cache,
+    const void* __restrict__ q, const float* __restrict__ q_scales,
+    const int8_t* __restrict__ k_cache,
     const int8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ ctx_lens, int ctx_cap, int num_pages, int n_q_heads,
@@ -91,7 +95,15 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
   for (int t = 0; t < 4; ++t)
     pg[t] = (16 * t < nvalid && pr[t] >= 0 && pr[t] < num_pages) ? pr[t] : 0;
   const size_t qrow = (size_t)s * n_q_heads + g * kGroup + min(w, kGroup - 1);
-  const uint2 qw = *reinterpret_cast<const uint2*>(q + qrow * kHeadDim + lane * 4);
+  uint2 qw = make_uint2(0u, 0u);
+  uint32_t qc = 0u;
+  float qsc = 0.f;
+  if (Q8) {
+    qc = *reinterpret_cast<const uint32_t*>(static_cast<const int8_t*>(q) + qrow * kHeadDim + lane * 4);
+    qsc = q_scales[qrow];
+  } else {
+    qw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(q) + qrow * kHeadDim + lane * 4);
+  }
   const int pl = (lane >> 4) == 0 ? pg[0] : (lane >> 4) == 1 ? pg[1] : (lane >> 4) == 2 ? pg[2] : pg[3];
   const size_t si = ((size_t)pl * n_kv_heads + g) * kPage + (lane & 15);
   const float sk_l = k_scale[si];
@@ -118,9 +130,10 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
 
   // Quantize the group's query rows (waves 0..5) and stage them with the scales in LDS.
   if (w < kGroup) {
-    float sc;
-    const uint32_t c = quantize4(bf16_to_f32(qw.x & 0xffffu), bf16_to_f32(qw.x >> 16),
-                                 bf16_to_f32(qw.y & 0xffffu), bf16_to_f32(qw.y >> 16), &sc);
+    float sc = qsc;
+    const uint32_t c = Q8 ? qc
+                          : quantize4(bf16_to_f32(qw.x & 0xffffu), bf16_to_f32(qw.x >> 16),
+                                      bf16_to_f32(qw.y & 0xffffu), bf16_to_f32(qw.y >> 16), &sc);
     *reinterpret_cast<uint32_t*>(&s_q[w][lane * 4]) = c;
     if (lane == 0) s_qs[w] = sc;
   }
@@ -360,7 +373,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   o[d] = acc / L;
 }
 
-int launch_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cache,
+int launch_decode(const void* q, const float* q_scales, const int8_t* k_cache, const int8_t* v_cache,
                   const float* k_scale, const float* v_scale, const int32_t* block_table,
                   int max_blocks, const int32_t* ctx_lens, int num_seqs, int max_ctx,
                   int num_pages, int n_q_heads, int n_kv_heads, float sm_scale, float* out,
@@ -371,10 +384,16 @@ int launch_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cach
   float* ws_o = ws + 2 * np;
   const long long cap = (long long)max_blocks * kPage;
   const int ctx_cap = (int)(cap < max_ctx ? cap : max_ctx);
-  hipLaunchKernelGGL(decode_split_kernel, dim3(max_parts, n_kv_heads, num_seqs), dim3(512), 0,
-                     stream, q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks,
-                     ctx_lens, ctx_cap, num_pages, n_q_heads, n_kv_heads, sm_scale * kLog2e, ws_m,
-                     ws_l, ws_o, max_parts, max_parts == 1 ? out : nullptr);
+  if (q_scales != nullptr)
+    hipLaunchKernelGGL(decode_split_kernel<1>, dim3(max_parts, n_kv_heads, num_seqs), dim3(512), 0,
+                       stream, q, q_scales, k_cache, v_cache, k_scale, v_scale, block_table,
+                       max_blocks, ctx_lens, ctx_cap, num_pages, n_q_heads, n_kv_heads,
+                       sm_scale * kLog2e, ws_m, ws_l, ws_o, max_parts, max_parts == 1 ? out : nullptr);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<0>, dim3(max_parts, n_kv_heads, num_seqs), dim3(512), 0,
+                       stream, q, q_scales, k_cache, v_cache, k_scale, v_scale, block_table,
+                       max_blocks, ctx_lens, ctx_cap, num_pages, n_q_heads, n_kv_heads,
+                       sm_scale * kLog2e, ws_m, ws_l, ws_o, max_parts, max_parts == 1 ? out : nullptr);
   int rc = check_launch("attn_decode stage 1");
   if (rc || max_parts == 1) return rc;
   hipLaunchKernelGGL(decode_merge_kernel<0>, dim3(kHeadDim / 64, n_q_heads, num_seqs), dim3(64), 0,
@@ -382,18 +401,19 @@ int launch_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cach
   return check_launch("attn_decode stage 2");
 }
 
-int launch_verify(const uint16_t* q, int nq, const int8_t* k_cache, const int8_t* v_cache,
+int launch_verify(const void* q, const float* q_scales, int nq, const int8_t* k_cache,
+                  const int8_t* v_cache,
                   const float* k_scale, const float* v_scale, const int32_t* block_table,
                   int max_blocks, const int32_t* ctx_lens, int num_seqs, int max_ctx,
                   int num_pages, int n_q_heads, int n_kv_heads, float sm_scale, float* out,
                   float* ws, int max_parts, hipStream_t stream) {
   if (nq == 1)  // one row: the one-row kernel (route by live rows)
-    return launch_decode(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, ctx_lens,
-                         num_seqs, max_ctx, num_pages, n_q_heads, n_kv_heads, sm_scale, out, ws,
-                         max_parts, stream);
+    return launch_decode(q, q_scales, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks,
+                         ctx_lens, num_seqs, max_ctx, num_pages, n_q_heads, n_kv_heads, sm_scale,
+                         out, ws, max_parts, stream);
   // several rows: one read of the K/V for all of them, the weighted sum of V on the int8
   // matrix cores with three digit planes per weight
-  return launch_decode_i8pv(3, kPart, q, nq, k_cache, v_cache, k_scale, v_scale, block_table,
+  return launch_decode_i8pv(3, kPart, q, q_scales, nq, k_cache, v_cache, k_scale, v_scale, block_table,
                             max_blocks, ctx_lens, num_seqs, max_ctx, num_pages, n_q_heads,
                             n_kv_heads, sm_scale, out, ws, stream);
 }

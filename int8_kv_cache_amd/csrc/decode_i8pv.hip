@@ -53,9 +53,11 @@ __device__ __forceinline__ uint32_t pack_byte(uint32_t x0, uint32_t x1, uint32_t
   return lo | hi;
 }
 
-template <int DIG, int WAVES>
+// Q8: the query arrives as int8 codes with fp32 scales (kv_produce's output).
+template <int DIG, int WAVES, int Q8>
 __global__ __launch_bounds__(WAVES * 64, 1) void split_i8pv_kernel(
-    const uint16_t* __restrict__ q, int nq, const int8_t* __restrict__ k_cache,
+    const void* __restrict__ q, const float* __restrict__ q_scales, int nq,
+    const int8_t* __restrict__ k_cache,
     const int8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ ctx_lens, int ctx_cap, int num_pages, int n_q_heads,
@@ -109,13 +111,19 @@ __global__ __launch_bounds__(WAVES * 64, 1) void split_i8pv_kernel(
   // This wave quantizes query rows w, w + WAVES, ... (my_rows of them).
   const int my_rows = n_rows > w ? (n_rows - w + WAVES - 1) / WAVES : 0;
   uint2 qw[kRowsPerWave];
+  float qsc[kRowsPerWave];
 #pragma unroll
   for (int k = 0; k < kRowsPerWave; ++k) {
     if (k < my_rows) {
       const int r = w + WAVES * k;
       const int qi = r / kGroup;
       const size_t row = ((size_t)s * nq + qi) * n_q_heads + g * kGroup + (r - kGroup * qi);
-      qw[k] = *reinterpret_cast<const uint2*>(q + row * kHeadDim + lane * 4);
+      if (Q8) {
+        qw[k].x = *reinterpret_cast<const uint32_t*>(static_cast<const int8_t*>(q) + row * kHeadDim + lane * 4);
+        qsc[k] = q_scales[row];
+      } else {
+        qw[k] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(q) + row * kHeadDim + lane * 4);
+      }
     }
   }
   const int pl = (lane >> 4) == 0 ? pg[0] : (lane >> 4) == 1 ? pg[1] : (lane >> 4) == 2 ? pg[2] : pg[3];
@@ -143,9 +151,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void split_i8pv_kernel(
   for (int k = 0; k < kRowsPerWave; ++k) {
     if (k < my_rows) {
       const int r = w + WAVES * k;
-      float sc;
-      const uint32_t c = quantize4(bf16_to_f32(qw[k].x & 0xffffu), bf16_to_f32(qw[k].x >> 16),
-                                   bf16_to_f32(qw[k].y & 0xffffu), bf16_to_f32(qw[k].y >> 16), &sc);
+      float sc = qsc[k];
+      const uint32_t c = Q8 ? qw[k].x
+                            : quantize4(bf16_to_f32(qw[k].x & 0xffffu), bf16_to_f32(qw[k].x >> 16),
+                                        bf16_to_f32(qw[k].y & 0xffffu), bf16_to_f32(qw[k].y >> 16), &sc);
       *reinterpret_cast<uint32_t*>(&s_q[r][lane * 4]) = c;
       if (lane == 0) s_qs[r] = sc;
     }
@@ -349,21 +358,28 @@ __global__ __launch_bounds__(WAVES * 64, 1) void split_i8pv_kernel(
 }
 
 template <int DIG, int WAVES>
-int launch_split(const uint16_t* q, int nq, const int8_t* k_cache, const int8_t* v_cache,
+int launch_split(const void* q, const float* q_scales, int nq, const int8_t* k_cache, const int8_t* v_cache,
                  const float* k_scale, const float* v_scale, const int32_t* block_table,
                  int max_blocks, const int32_t* ctx_lens, int ctx_cap, int num_seqs,
                  int num_pages, int n_q_heads, int n_kv_heads, float qk_scale_log2, float* ws_m,
                  float* ws_l, float* ws_o, int max_parts, float* out, hipStream_t stream) {
-  hipLaunchKernelGGL((split_i8pv_kernel<DIG, WAVES>), dim3(max_parts, n_kv_heads, num_seqs),
-                     dim3(WAVES * 64), 0, stream, q, nq, k_cache, v_cache, k_scale, v_scale,
-                     block_table, max_blocks, ctx_lens, ctx_cap, num_pages, n_q_heads, n_kv_heads,
-                     qk_scale_log2, ws_m, ws_l, ws_o, max_parts, out);
+  if (q_scales != nullptr)
+    hipLaunchKernelGGL((split_i8pv_kernel<DIG, WAVES, 1>), dim3(max_parts, n_kv_heads, num_seqs),
+                       dim3(WAVES * 64), 0, stream, q, q_scales, nq, k_cache, v_cache, k_scale,
+                       v_scale, block_table, max_blocks, ctx_lens, ctx_cap, num_pages, n_q_heads,
+                       n_kv_heads, qk_scale_log2, ws_m, ws_l, ws_o, max_parts, out);
+  else
+    hipLaunchKernelGGL((split_i8pv_kernel<DIG, WAVES, 0>), dim3(max_parts, n_kv_heads, num_seqs),
+                       dim3(WAVES * 64), 0, stream, q, q_scales, nq, k_cache, v_cache, k_scale,
+                       v_scale, block_table, max_blocks, ctx_lens, ctx_cap, num_pages, n_q_heads,
+                       n_kv_heads, qk_scale_log2, ws_m, ws_l, ws_o, max_parts, out);
   return check_launch("int8-PV decode stage 1");
 }
 
 }  // namespace
 
-int launch_decode_i8pv(int digits, int part_rows, const uint16_t* q, int nq, const int8_t* k_cache,
+int launch_decode_i8pv(int digits, int part_rows, const void* q, const float* q_scales, int nq,
+                       const int8_t* k_cache,
                        const int8_t* v_cache, const float* k_scale, const float* v_scale,
                        const int32_t* block_table, int max_blocks, const int32_t* ctx_lens,
                        int num_seqs, int max_ctx, int num_pages, int n_q_heads, int n_kv_heads,
@@ -378,7 +394,7 @@ int launch_decode_i8pv(int digits, int part_rows, const uint16_t* q, int nq, con
   const float qs = sm_scale * kLog2e;
   float* direct = max_parts == 1 ? out : nullptr;  // one partition: no merge stage
   int rc;
-#define I8PV_ARGS q, nq, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, ctx_lens, \
+#define I8PV_ARGS q, q_scales, nq, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, ctx_lens, \
                   ctx_cap, num_seqs, num_pages, n_q_heads, n_kv_heads, qs, ws_m, ws_l, ws_o,   \
                   max_parts, direct, stream
   if (digits == 1) {

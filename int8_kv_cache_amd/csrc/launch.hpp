@@ -14,14 +14,21 @@ int check_launch(const char* what);
 int launch_kv_quant_write(const void* k, const void* v, int in_bf16, int n_tokens, int n_kv_heads,
                           const int32_t* slots, int8_t* k_cache, int8_t* v_cache, float* k_scale,
                           float* v_scale, int num_pages, hipStream_t stream);
+int launch_kv_produce(const void* q, const void* k, const void* v, int in_bf16, int n_tokens,
+                      int n_q_heads, int n_kv_heads, const int32_t* positions, const float* cos_sin,
+                      int rotary_dim, int max_pos, const int32_t* slots, int8_t* k_cache,
+                      int8_t* v_cache, float* k_scale, float* v_scale, int num_pages,
+                      int8_t* q_codes, float* q_scales, hipStream_t stream);
 int launch_q_quant(const uint16_t* q, int n_rows, int8_t* codes, float* scales,
                    hipStream_t stream);
-int launch_decode(const uint16_t* q, const int8_t* k_cache, const int8_t* v_cache,
+// q: bf16 rows to quantize (q_scales == nullptr) or int8 codes with q_scales (kv_produce).
+int launch_decode(const void* q, const float* q_scales, const int8_t* k_cache, const int8_t* v_cache,
                   const float* k_scale, const float* v_scale, const int32_t* block_table,
                   int max_blocks, const int32_t* ctx_lens, int num_seqs, int max_ctx,
                   int num_pages, int n_q_heads, int n_kv_heads, float sm_scale, float* out,
                   float* ws, int max_parts, hipStream_t stream);
-int launch_verify(const uint16_t* q, int nq, const int8_t* k_cache, const int8_t* v_cache,
+int launch_verify(const void* q, const float* q_scales, int nq, const int8_t* k_cache,
+                  const int8_t* v_cache,
                   const float* k_scale, const float* v_scale, const int32_t* block_table,
                   int max_blocks, const int32_t* ctx_lens, int num_seqs, int max_ctx,
                   int num_pages, int n_q_heads, int n_kv_heads, float sm_scale, float* out,
@@ -29,12 +36,14 @@ int launch_verify(const uint16_t* q, int nq, const int8_t* k_cache, const int8_t
 int launch_merge(const float* ws_m, const float* ws_l, const float* ws_o, const int32_t* ctx_lens,
                  int ctx_cap, int num_seqs, int nq, int n_q_heads, int max_parts, int part_rows,
                  float* out, hipStream_t stream);
-int launch_decode_i8pv(int digits, int part_rows, const uint16_t* q, int nq, const int8_t* k_cache,
+int launch_decode_i8pv(int digits, int part_rows, const void* q, const float* q_scales, int nq,
+                       const int8_t* k_cache,
                        const int8_t* v_cache, const float* k_scale, const float* v_scale,
                        const int32_t* block_table, int max_blocks, const int32_t* ctx_lens,
                        int num_seqs, int max_ctx, int num_pages, int n_q_heads, int n_kv_heads,
                        float sm_scale, float* out, float* ws, hipStream_t stream);
-int launch_prefill(const uint16_t* q, int n_new, const int8_t* k_cache, const int8_t* v_cache,
+int launch_prefill(const void* q, const float* q_scales, int n_new, const int8_t* k_cache,
+                   const int8_t* v_cache,
                    const float* k_scale, const float* v_scale, const int32_t* block_table,
                    int ctx, int causal, int num_pages, int n_q_heads, int n_kv_heads,
                    float sm_scale, float* out, hipStream_t stream);

@@ -236,8 +236,12 @@ __device__ __forceinline__ void block_step(
   lds_barrier();
 }
 
+// Q8: the query arrives as int8 codes with fp32 scales (kv_produce's output) instead of
+// bf16 rows to quantize.
+template <int Q8>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
-    const uint16_t* __restrict__ q, int n_new, const int8_t* __restrict__ k_cache,
+    const void* __restrict__ q, const float* __restrict__ q_scales, int n_new,
+    const int8_t* __restrict__ k_cache,
     const int8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int ctx,
     int causal, int num_pages, int n_q_heads, int n_kv_heads, float qk_scale_log2,
@@ -287,16 +291,24 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
   int8_t* qrows = &s_q[hl * kPfTok + 16 * half][0];
   {
     uint2 qw[16];
+    float qsc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int tok = min(t0 + 16 * half + r, n_new - 1);
-      qw[r] = *reinterpret_cast<const uint2*>(q + ((size_t)tok * n_q_heads + h) * kHeadDim + lane * 4);
+      const size_t row = (size_t)tok * n_q_heads + h;
+      if (Q8) {
+        qw[r].x = *reinterpret_cast<const uint32_t*>(static_cast<const int8_t*>(q) + row * kHeadDim + lane * 4);
+        qsc[r] = q_scales[row];
+      } else {
+        qw[r] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(q) + row * kHeadDim + lane * 4);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float sc;
-      uint32_t c = quantize4(bf16_to_f32(qw[r].x & 0xffffu), bf16_to_f32(qw[r].x >> 16),
-                             bf16_to_f32(qw[r].y & 0xffffu), bf16_to_f32(qw[r].y >> 16), &sc);
+      float sc = qsc[r];
+      uint32_t c = Q8 ? qw[r].x
+                      : quantize4(bf16_to_f32(qw[r].x & 0xffffu), bf16_to_f32(qw[r].x >> 16),
+                                  bf16_to_f32(qw[r].y & 0xffffu), bf16_to_f32(qw[r].y >> 16), &sc);
       const bool live = 16 * half + r < nq;
       *reinterpret_cast<uint32_t*>(qrows + r * kQStride + lane * 4) = live ? c : 0u;
       if (lane == 0) s_qs[hl][16 * half + r] = live ? sc : 0.f;
@@ -347,7 +359,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
   }
 }
 
-int launch_prefill(const uint16_t* q, int n_new, const int8_t* k_cache, const int8_t* v_cache,
+int launch_prefill(const void* q, const float* q_scales, int n_new, const int8_t* k_cache,
+                   const int8_t* v_cache,
                    const float* k_scale, const float* v_scale, const int32_t* block_table,
                    int ctx, int causal, int num_pages, int n_q_heads, int n_kv_heads,
                    float sm_scale, float* out, hipStream_t stream) {
@@ -358,10 +371,16 @@ int launch_prefill(const uint16_t* q, int n_new, const int8_t* k_cache, const in
   const long long n_wg = xcd_per_head > 0
                              ? (long long)kXcds * ((n_qb + xcd_per_head - 1) / xcd_per_head)
                              : (long long)n_qb * n_kv_heads;
-  hipLaunchKernelGGL(prefill_chunk_kernel, dim3((unsigned)n_wg), dim3(kPfThreads), 0, stream, q,
-                     n_new, k_cache, v_cache, k_scale, v_scale, block_table, ctx, causal,
-                     num_pages, n_q_heads, n_kv_heads, sm_scale * kLog2e, out, n_qb,
-                     xcd_per_head);
+  if (q_scales != nullptr)
+    hipLaunchKernelGGL(prefill_chunk_kernel<1>, dim3((unsigned)n_wg), dim3(kPfThreads), 0, stream,
+                       q, q_scales, n_new, k_cache, v_cache, k_scale, v_scale, block_table, ctx,
+                       causal, num_pages, n_q_heads, n_kv_heads, sm_scale * kLog2e, out, n_qb,
+                       xcd_per_head);
+  else
+    hipLaunchKernelGGL(prefill_chunk_kernel<0>, dim3((unsigned)n_wg), dim3(kPfThreads), 0, stream,
+                       q, q_scales, n_new, k_cache, v_cache, k_scale, v_scale, block_table, ctx,
+                       causal, num_pages, n_q_heads, n_kv_heads, sm_scale * kLog2e, out, n_qb,
+                       xcd_per_head);
   return check_launch("attn_prefill_chunk");
 }
 

@@ -1,7 +1,9 @@
-// kv_quant_write and q_quant kernels: per-row absmax/127 int8 quantization of new K/V
-// rows written straight into the paged cache, and of bf16 query rows.
+// kv_quant_write, kv_produce and q_quant kernels: per-row absmax/127 int8 quantization
+// of new K/V rows written straight into the paged cache (kv_produce first rotates K and
+// Q by RoPE and also quantizes Q), and of bf16 query rows.
 // ("INT8 KV and INT8 MMAC attention on a gfx936 DCU", §2.1 rule, §2.2 fused producer:
-// absmax, scale, quantize, paged INT8 write and scale write in one kernel.)
+// read Q/K/V, RoPE on Q/K, absmax, scale, quantize, paged INT8 write and scale write in
+// one kernel, with no high-precision Q/K written back.)
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -21,18 +23,62 @@ __device__ __forceinline__ void load_row4(const void* base, size_t row, int lane
   }
 }
 
+// RoPE on one row held 4 dims per lane (lane l: dims 4l..4l+3). Pair (i, i + rd/2) of
+// the first rd dims turns by the angle whose cos and sin are cs[i] and cs[rd/2 + i]; rd is
+// a multiple of 8, so a lane's 4 dims are all rotated or all passed through and all in
+// one half. Every product and sum is rounded on its own (no contraction into fma), the
+// fp32 rule the results are defined by.
+__device__ __forceinline__ float rot_first(float a, float c, float b, float s) {
+#pragma clang fp contract(off)
+  return a * c - b * s;
+}
+__device__ __forceinline__ float rot_second(float b, float c, float a, float s) {
+#pragma clang fp contract(off)
+  return b * c + a * s;
+}
+__device__ __forceinline__ void rope4(float* x, const float* __restrict__ cs, int rd, int lane) {
+  const int half = rd >> 1;
+  const int d0 = lane * 4;
+  const bool in = d0 < rd, first = d0 < half;
+  const int partner = in ? (first ? lane + (half >> 2) : lane - (half >> 2)) : lane;
+  float y[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) y[j] = __shfl(x[j], partner);
+  if (in) {
+    const int i0 = first ? d0 : d0 - half;
+    const float4 c = *reinterpret_cast<const float4*>(cs + i0);
+    const float4 sn = *reinterpret_cast<const float4*>(cs + half + i0);
+    const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      x[j] = first ? rot_first(x[j], cc[j], y[j], ss[j]) : rot_second(x[j], cc[j], y[j], ss[j]);
+  }
+}
+
 // Workgroup = (16 consecutive tokens, KV head): wave w quantizes the K and V rows of
 // tokens 4w..4w+3 of the group (row loads issued before anything waits). When the 16
 // tokens fill one whole page in order (slots s0..s0+15, s0 % 16 == 0, the common case of
 // prefill chunks and bulk fills) the workgroup assembles the page's dim-major V block
 // in LDS and writes K, V and the scales as whole 16-byte runs; otherwise every token is
 // scattered to its own slot.
-template <int IN_BF16>
+// With PRODUCE (kv_produce) the K rows are rotated by their token's position first, and
+// the workgroup also rotates and quantizes the query rows of the KV head's group for its
+// 16 tokens (wave w: tokens 4w..4w+3, all 6 heads), codes row-major into q_codes.
+struct Produce {
+  const void* q;
+  const int32_t* positions;
+  const float* cos_sin;
+  int rotary_dim, max_pos, n_q_heads;
+  int8_t* q_codes;
+  float* q_scales;
+};
+
+template <int IN_BF16, int PRODUCE>
 __global__ __launch_bounds__(256) void kv_quant_write_kernel(
     const void* __restrict__ k, const void* __restrict__ v, int n_tokens, int n_kv_heads,
     const int32_t* __restrict__ slots, int8_t* __restrict__ k_cache,
     int8_t* __restrict__ v_cache, float* __restrict__ k_scale, float* __restrict__ v_scale,
-    long long n_slots) {
+    long long n_slots, Produce pr) {
   const int grp = blockIdx.x, head = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int tok0 = grp * 16;
@@ -59,12 +105,54 @@ __global__ __launch_bounds__(256) void kv_quant_write_kernel(
     load_row4<IN_BF16>(v, row, lane, vx[i]);
     myslot[i] = tok0 + 4 * w + i < n_tokens ? slots[tok0 + 4 * w + i] : -1;
   }
+  // Query rows of the group for this wave's tokens, loaded with the K/V rows (one round
+  // trip); tokens past the batch re-read the last one and are not stored.
+  float qx[PRODUCE ? 4 : 1][kGroup][4];
+  const bool want_q = PRODUCE && pr.q_codes != nullptr;
+  if (want_q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = min(tok0 + 4 * w + i, n_tokens - 1);
+#pragma unroll
+      for (int hh = 0; hh < kGroup; ++hh)
+        load_row4<IN_BF16>(pr.q, (size_t)t * pr.n_q_heads + head * kGroup + hh, lane,
+                           qx[PRODUCE ? i : 0][hh]);
+    }
+  }
+  const float* cs_row[4] = {nullptr, nullptr, nullptr, nullptr};  // RoPE rows of the tokens
+  if (PRODUCE && pr.rotary_dim > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = min(tok0 + 4 * w + i, n_tokens - 1);
+      const int pos = min(max(pr.positions[t], 0), pr.max_pos - 1);  // clamped: memory-safe
+      cs_row[i] = pr.cos_sin + (size_t)pos * pr.rotary_dim;
+      rope4(kx[i], cs_row[i], pr.rotary_dim, lane);
+    }
+  }
   uint32_t kq[4], vq[4];
   float ks[4], vs[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     kq[i] = quantize4(kx[i][0], kx[i][1], kx[i][2], kx[i][3], &ks[i]);
     vq[i] = quantize4(vx[i][0], vx[i][1], vx[i][2], vx[i][3], &vs[i]);
+  }
+  if (want_q) {
+    // The group's query rows of this wave's tokens: rotate, quantize, store.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = tok0 + 4 * w + i;
+      if (t >= n_tokens) break;  // whole wave
+#pragma unroll
+      for (int hh = 0; hh < kGroup; ++hh) {
+        float* xr = qx[PRODUCE ? i : 0][hh];
+        if (pr.rotary_dim > 0) rope4(xr, cs_row[i], pr.rotary_dim, lane);
+        float sc;
+        const uint32_t c = quantize4(xr[0], xr[1], xr[2], xr[3], &sc);
+        const size_t row = (size_t)t * pr.n_q_heads + head * kGroup + hh;
+        *reinterpret_cast<uint32_t*>(pr.q_codes + row * kHeadDim + lane * 4) = c;
+        if (lane == 0) pr.q_scales[row] = sc;
+      }
+    }
   }
   __syncthreads();
   if (s_run) {
@@ -136,13 +224,31 @@ int launch_kv_quant_write(const void* k, const void* v, int in_bf16, int n_token
                           float* v_scale, int num_pages, hipStream_t stream) {
   const dim3 grid((n_tokens + 15) / 16, n_kv_heads), block(256);
   const long long n_slots = (long long)num_pages * kPage;
+  const Produce none{nullptr, nullptr, nullptr, 0, 1, 0, nullptr, nullptr};
   if (in_bf16)
-    hipLaunchKernelGGL(kv_quant_write_kernel<1>, grid, block, 0, stream, k, v, n_tokens,
-                       n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots);
+    hipLaunchKernelGGL((kv_quant_write_kernel<1, 0>), grid, block, 0, stream, k, v, n_tokens,
+                       n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots, none);
   else
-    hipLaunchKernelGGL(kv_quant_write_kernel<0>, grid, block, 0, stream, k, v, n_tokens,
-                       n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots);
+    hipLaunchKernelGGL((kv_quant_write_kernel<0, 0>), grid, block, 0, stream, k, v, n_tokens,
+                       n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots, none);
   return check_launch("kv_quant_write");
+}
+
+int launch_kv_produce(const void* q, const void* k, const void* v, int in_bf16, int n_tokens,
+                      int n_q_heads, int n_kv_heads, const int32_t* positions, const float* cos_sin,
+                      int rotary_dim, int max_pos, const int32_t* slots, int8_t* k_cache,
+                      int8_t* v_cache, float* k_scale, float* v_scale, int num_pages,
+                      int8_t* q_codes, float* q_scales, hipStream_t stream) {
+  const dim3 grid((n_tokens + 15) / 16, n_kv_heads), block(256);
+  const long long n_slots = (long long)num_pages * kPage;
+  const Produce pr{q, positions, cos_sin, rotary_dim, max_pos, n_q_heads, q_codes, q_scales};
+  if (in_bf16)
+    hipLaunchKernelGGL((kv_quant_write_kernel<1, 1>), grid, block, 0, stream, k, v, n_tokens,
+                       n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots, pr);
+  else
+    hipLaunchKernelGGL((kv_quant_write_kernel<0, 1>), grid, block, 0, stream, k, v, n_tokens,
+                       n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots, pr);
+  return check_launch("kv_produce");
 }
 
 int launch_q_quant(const uint16_t* q, int n_rows, int8_t* codes, float* scales,

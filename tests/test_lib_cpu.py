@@ -172,6 +172,33 @@ def test_attn_decode_int8p_validation():
     assert call(9, 0) == C["I8A_OK"]
 
 
+def test_kv_produce_and_q8_validation():
+    C = _codes()
+    L = m.lib()
+    base = [FAKE, FAKE, FAKE, 1, 4, 24, 4, 256, FAKE, FAKE, 64, 100, FAKE, FAKE, FAKE, FAKE, FAKE,
+            10, FAKE, FAKE, None]
+
+    def call(i=None, val=None):
+        a = list(base)
+        if i is not None:
+            a[i] = val
+        return L.kv_produce(*a)
+
+    assert call(10, 12) == C["I8A_EINVAL"]              # rotary_dim not a multiple of 8
+    assert call(10, 264) == C["I8A_EINVAL"]             # rotary_dim > head_dim
+    assert call(9, None) == C["I8A_EINVAL"]             # RoPE without a table
+    assert call(11, 0) == C["I8A_EINVAL"]               # ... or without positions range
+    assert call(18, None) == C["I8A_EINVAL"]            # q_codes without q_scales
+    assert call(5, 12) == C["I8A_EUNSUPPORTED"]         # group of 3
+    assert call(3, 7) == C["I8A_EINVAL"]                # dtype
+    assert call(4, 0) == C["I8A_OK"]                    # no tokens
+    dec = [FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 100, 10, 24, 4, 256, 0.0625,
+           FAKE, FAKE, 1 << 20, None]
+    assert L.attn_decode_q8(*dec) == C["I8A_EINVAL"]     # codes without scales
+    pf = [FAKE, None, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 1, 16, 24, 4, 256, 0.0625, FAKE, None]
+    assert L.attn_prefill_chunk_q8(*pf) == C["I8A_EINVAL"]
+
+
 def test_attn_prefill_validation():
     C = _codes()
     L = m.lib()
