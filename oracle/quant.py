@@ -24,6 +24,16 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """Round finite fp32 values to the nearest bf16 (8 significant bits), ties to even;
+    returns the bf16 bit patterns (uint16). Evaluated as m * 2^e with 0.5 <= |m| < 1:
+    rint(m * 2^8) / 2^8 is exact in float64, so the only rounding is rint's."""
+    x = np.asarray(x, dtype=np.float32)
+    m, e = np.frexp(x.astype(np.float64))
+    r = np.ldexp(np.rint(m * 256.0) / 256.0, e).astype(np.float32)   # exact: <= 9 bits
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
 def quantize_rows(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """Quantize the last axis of x (fp32). Returns (codes int8, scales fp32 [x.shape[:-1]])."""
     x = np.asarray(x, dtype=np.float32)

@@ -16,7 +16,11 @@ Readings where the article leaves a step open:
     x_j' = fl(fl(x_j c_i) + fl(x_i s_i)), j = i + rd/2. The rotated rows are then
     quantized with the rule of `quant.quantize_rows`, so codes and scales are bit-exact
     functions of the inputs;
-  * inputs are fp32, or bf16 widened exactly to fp32.
+  * inputs are fp32, or bf16 widened exactly to fp32;
+  * first chunk ("INT8 KV and INT8 MMAC attention on a gfx936 DCU", §3.1): a chunk with
+    no history runs a high-precision attention while the producer still writes the int8
+    K/V; that attention reads the rotated Q and K rounded to bf16 (nearest, ties to even)
+    and the input V, the bf16 rows a high-precision kernel takes.
 """
 from __future__ import annotations
 
@@ -57,3 +61,16 @@ def produce(q, k, v, positions, cos_sin, rotary_dim, slots, cache):
     vc, vs = quant.quantize_rows(v)
     paged.write_rows(cache, slots, kc, ks, vc, vs)
     return qc, qs
+
+
+def produce_first_chunk(q, k, v, positions, cos_sin, rotary_dim, slots, cache):
+    """The producer of a chunk with no history: the paged int8 K/V write of `produce`,
+    and the rotated Q and K rows rounded to bf16 for the high-precision attention.
+    Returns (q_rot bf16 bits [T,Hq,D], k_rot bf16 bits [T,Hkv,D])."""
+    pos = np.asarray(positions, dtype=np.int64)
+    qr = rope_rows(q, pos[:, None], cos_sin, rotary_dim)
+    kr = rope_rows(k, pos[:, None], cos_sin, rotary_dim)
+    kc, ks = quant.quantize_rows(kr)
+    vc, vs = quant.quantize_rows(v)
+    paged.write_rows(cache, slots, kc, ks, vc, vs)
+    return quant.f32_to_bf16_rne(qr), quant.f32_to_bf16_rne(kr)

@@ -197,3 +197,22 @@ def test_negative_slot_skips_row():
     kc = np.ones((2, 1, 256), np.int8); s = np.ones((2, 1), np.float32)
     paged.write_rows(cache, np.array([-1, 3]), kc, s, kc, s)
     assert np.count_nonzero(cache[0]) == 256 and cache[2][3] == 1.0 and cache[2][0] == 0.0
+
+
+def test_bf16_rounding_closed_forms():
+    cases = {
+        1.0: 0x3F80, -2.5: 0xC020,                        # exactly representable
+        1.0 + 2.0 ** -8: 0x3F80,                          # halfway 1 .. 1+2^-7: to even (1)
+        1.0 + 3 * 2.0 ** -8: 0x3F82,                      # halfway 1+2^-7 .. 1+2^-6: to even
+        1.0 + 2.0 ** -8 + 2.0 ** -20: 0x3F81,             # just above halfway: up
+        3.0e-38: 0x0123,                                  # near the bottom of the normals
+    }
+    for x, bits in cases.items():
+        got = int(quant.f32_to_bf16_rne(np.array([x], np.float32))[0])
+        assert got == bits, (x, hex(got), hex(bits))
+
+
+def test_bf16_rounding_agrees_with_the_bit_trick():
+    """The input generators round with an integer-add trick; the two agree on normals."""
+    x = np.random.default_rng(13).standard_normal(100000).astype(np.float32) * np.float32(50.0)
+    assert np.array_equal(quant.f32_to_bf16_rne(x), workloads.f32_to_bf16_bits(x))

@@ -69,3 +69,21 @@ def test_producer_is_rope_then_quantize_then_write():
     # Q codes are the quantized rotated rows; dequantized they sit within half a code of them
     qr = rope.rope_rows(q, pos[:, None], table, 256)
     assert np.all(np.abs(quant.dequantize(qc, qs) - qr) <= 0.5001 * qs[..., None])
+
+
+def test_first_chunk_producer_writes_the_same_cache_and_rounds_the_rotated_rows():
+    case = workloads.make_producer_case(6, 33, start=0)
+    q, k, v = case.data()
+    table = case.table()
+    c1 = paged.alloc_cache(case.num_pages, 4, 0, 0.0)
+    c2 = paged.alloc_cache(case.num_pages, 4, 0, 0.0)
+    rope.produce(q, k, v, case.positions, table, 256, case.slots, c1)
+    qb, kb = rope.produce_first_chunk(q, k, v, case.positions, table, 256, case.slots, c2)
+    for a, b in zip(c1, c2):
+        assert np.array_equal(a, b)
+    pos = case.positions.astype(np.int64)[:, None]
+    qr = rope.rope_rows(q, pos, table, 256)
+    back = quant.bf16_bits_to_f32(qb)
+    # nearest bf16: within half a bf16 ulp (2^-9 relative) of the fp32 rotated value
+    assert np.all(np.abs(back - qr) <= np.abs(qr) * 2.0 ** -9 + 1e-30)
+    assert np.array_equal(kb, quant.f32_to_bf16_rne(rope.rope_rows(k, pos, table, 256)))
