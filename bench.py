@@ -337,6 +337,24 @@ def main():
     res["produce_2048"] = {"us": round(prod_us, 3), "bytes": prod_bytes,
                            "hbm_GBps": round(prod_bytes / (prod_us * 1e-6) / 1e9, 1),
                            "one_token_us_graph": round(tok1, 3)}
+    # the high-precision route of a chunk with no history: bf16 attention of the chunk's
+    # 2,048 rotated rows over themselves (causal)
+    qr, kr = lib.kv_produce(qb, kb, vb, pos_t - pos0, rope_tab, s_chunk, pcache, rotated_bf16=True)
+    out_fc = torch.empty_like(out_pf)
+    for _ in range(3):
+        lib.attn_chunk_bf16(qr, kr, vb, True, out=out_fc)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        lib.attn_chunk_bf16(qr, kr, vb, True, out=out_fc)
+    e1.record()
+    torch.cuda.synchronize()
+    fc_ms = e0.elapsed_time(e1) / 10
+    n_fc = pf.n_new
+    fc_flops = pf.n_q_heads * n_fc * (n_fc + 1) // 2 * 4 * pf.head_dim
+    res["first_chunk_bf16_2048"] = {"ms": round(fc_ms, 4), "flops": fc_flops,
+                                    "TFLOPs": round(fc_flops / (fc_ms * 1e-3) / 1e12, 1),
+                                    "bf16_mfma_frac": round(fc_flops / (fc_ms * 1e-3) / 2.5e15, 4)}
     res["verify_ctx32768"] = verify
     res["decode_int8p_ctx32768"] = {"us": round(i8p_us, 3), "partition": part,
                                     "hbm_GBps": round(dec_b / (i8p_us * 1e-6) / 1e9, 1)}

@@ -126,15 +126,57 @@ int kv_quant_write(const void* k, const void* v, int in_dtype,
  *                and sum rounded on its own: x_i' = x_i c - x_j s, x_j' = x_j c + x_i s.
  *  q_codes       int8 [n_tokens][n_q_heads][head_dim] and q_scales fp32
  *                [n_tokens][n_q_heads]: the rotated Q rows quantized (the *_q8 attention
- *                entry points take them as they are).
- *  V rows are not rotated. Codes and scales are bit-exact functions of the inputs and
- *  the table. */
+ *                entry points take them as they are); both NULL: not produced.
+ *  q_rot, k_rot  bf16 [n_tokens][n_q_heads][head_dim] / [n_tokens][n_kv_heads][head_dim]:
+ *                the rotated Q and K rows rounded to bf16 (nearest, ties to even), for the
+ *                high-precision attention of a chunk with no history [DCU §3.1]; NULL: not
+ *                written. q must be given when q_codes or q_rot is.
+ *  V rows are not rotated. Codes, scales and bf16 rows are bit-exact functions of the
+ *  inputs and the table. */
 int kv_produce(const void* q, const void* k, const void* v, int in_dtype,
                int n_tokens, int n_q_heads, int n_kv_heads, int head_dim,
                const int32_t* positions, const float* cos_sin, int rotary_dim,
                int max_position, const int32_t* slot_mapping,
                int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale,
-               int num_pages, int8_t* q_codes, float* q_scales, void* stream);
+               int num_pages, int8_t* q_codes, float* q_scales,
+               uint16_t* q_rot, uint16_t* k_rot, void* stream);
+
+/* attn_chunk_bf16 -- high-precision causal (or full) attention of a chunk over its own
+ * rows: q [n][n_q_heads][head_dim], k, v [n][n_kv_heads][head_dim], all bf16 and
+ * contiguous; query t sees keys 0..t (causal) or all n.
+ * [DCU §3.1: the first prefill chunk has no history and keeps a high-precision attention
+ *  while the producer writes its K/V as int8.]
+ *  Scores are bf16 x bf16 products summed in fp32; the softmax runs in fp32; the weights
+ *  multiply V as two bf16 terms (16 significant bits) with fp32 accumulation, so the
+ *  output meets the fp32-class bound (1e-4 * max|V|) against exact attention on the
+ *  same bf16 rows.
+ *  out           fp32 [n][n_q_heads][head_dim]. n == 0 is a no-op. */
+int attn_chunk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n,
+                    int causal, int n_q_heads, int n_kv_heads, int head_dim,
+                    float sm_scale, float* out, void* stream);
+
+/* Bytes of scratch prefill_step needs: the larger of the rotated bf16 Q and K rows
+ * (n_new * (n_q_heads + n_kv_heads) * head_dim * 2) and the int8 Q codes with scales
+ * (n_new * n_q_heads * (head_dim + 4)), rounded up to 256. 0 for invalid arguments. */
+size_t prefill_step_workspace_bytes(int n_new, int n_q_heads, int n_kv_heads, int head_dim);
+
+/* prefill_step -- one prefill chunk end to end, routed by its history [DCU §3.1, §3.2]:
+ * the producer (RoPE, quantization, paged K/V write) runs first, then
+ *  - context_len == n_new (no history): attn_chunk_bf16 on the rotated bf16 rows;
+ *  - otherwise: attn_prefill_chunk_q8 on the int8 cache with the producer's Q codes
+ *    (the history exists only as int8).
+ *  q, k, v       bf16 [n_new][heads][head_dim] as projected (before RoPE).
+ *  positions, cos_sin, rotary_dim, max_position, slot_mapping, caches: as for kv_produce.
+ *  block_table, context_len: as for attn_prefill_chunk (context_len counts the chunk).
+ *  workspace     >= prefill_step_workspace_bytes(...), 256-byte aligned.
+ *  out           fp32 [n_new][n_q_heads][head_dim]. */
+int prefill_step(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n_new,
+                 const int32_t* positions, const float* cos_sin, int rotary_dim,
+                 int max_position, const int32_t* slot_mapping,
+                 int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale,
+                 int num_pages, const int32_t* block_table, int context_len,
+                 int n_q_heads, int n_kv_heads, int head_dim, float sm_scale, float* out,
+                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* q_quant -- quantize bf16 query rows with the same rule [DCU §2.2: the query is
  * quantized once per token and head]. The attention entry points do this internally

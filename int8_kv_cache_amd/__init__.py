@@ -18,7 +18,8 @@ import torch
 __all__ = ["lib", "PagedCache", "alloc_cache", "kv_quant_write", "q_quant", "attn_decode",
            "attn_decode_workspace_bytes", "attn_verify", "attn_verify_workspace_bytes",
            "attn_decode_int8p", "attn_decode_int8p_workspace_bytes", "attn_decode_partition_rows",
-           "attn_prefill_chunk", "kv_produce", "Int8AttnError",
+           "attn_prefill_chunk", "kv_produce", "attn_chunk_bf16", "prefill_step",
+           "prefill_step_workspace_bytes", "Int8AttnError",
            "HEAD_DIM", "PAGE", "PARTITION", "EXPORTED_SYMBOLS"]
 
 HEAD_DIM = 256
@@ -27,7 +28,8 @@ PARTITION = 512
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint8attn.so")
 EXPORTED_SYMBOLS = ("int8attn_last_error", "int8attn_version", "kv_quant_write", "kv_produce",
                     "q_quant", "attn_decode_q8", "attn_verify_q8", "attn_decode_int8p_q8",
-                    "attn_prefill_chunk_q8",
+                    "attn_prefill_chunk_q8", "attn_chunk_bf16", "prefill_step_workspace_bytes",
+                    "prefill_step",
                     "attn_decode_workspace_bytes", "attn_decode", "attn_verify_workspace_bytes",
                     "attn_verify", "attn_decode_partition_rows",
                     "attn_decode_int8p_workspace_bytes", "attn_decode_int8p",
@@ -45,7 +47,14 @@ _SIGNATURES = {
                                 _c_void, _c_void, _c_void, _c_void, _c_int, _c_void]),
     "kv_produce": (_c_int, [_c_void, _c_void, _c_void, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_void, _c_void, _c_int, _c_int, _c_void, _c_void, _c_void, _c_void,
-                            _c_void, _c_int, _c_void, _c_void, _c_void]),
+                            _c_void, _c_int, _c_void, _c_void, _c_void, _c_void, _c_void]),
+    "attn_chunk_bf16": (_c_int, [_c_void, _c_void, _c_void, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                 _c_float, _c_void, _c_void]),
+    "prefill_step_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
+    "prefill_step": (_c_int, [_c_void, _c_void, _c_void, _c_int, _c_void, _c_void, _c_int, _c_int,
+                              _c_void, _c_void, _c_void, _c_void, _c_void, _c_int, _c_void, _c_int,
+                              _c_int, _c_int, _c_int, _c_float, _c_void, _c_void, _c_size,
+                              _c_void]),
     "q_quant": (_c_int, [_c_void, _c_int, _c_int, _c_void, _c_void, _c_void]),
     "attn_decode_q8": (_c_int, [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void, _c_void,
                                 _c_int, _c_void, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -179,12 +188,12 @@ def kv_quant_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
 
 def kv_produce(q, k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
                cos_sin: torch.Tensor | None, slot_mapping: torch.Tensor, cache,
-               rotary_dim: int | None = None, stream=None):
+               rotary_dim: int | None = None, stream=None, rotated_bf16: bool = False):
     """Fused producer: RoPE on q [T, Hq, 256] and k [T, Hkv, 256] (fp32 or bf16, one dtype)
     from the table cos_sin [max_pos, rotary_dim] (cos half, then sin half), quantize q, k,
     v, write k/v into the paged cache at their slots. Returns (q_codes int8 [T, Hq, 256],
-    q_scales fp32 [T, Hq]), or None when q is None. rotary_dim defaults to the table width
-    (0: no rotation)."""
+    q_scales fp32 [T, Hq]), or None when q is None; with rotated_bf16 it returns the
+    rotated (q, k) rows in bf16 instead. rotary_dim defaults to the table width (0: none)."""
     if k.dim() != 3 or k.shape != v.shape or k.dtype != v.dtype:
         raise ValueError("k and v must both be [T, Hkv, head_dim] of one dtype")
     T, H, D = k.shape
@@ -198,20 +207,84 @@ def kv_produce(q, k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
     rd = (cos_sin.shape[1] if cos_sin is not None else 0) if rotary_dim is None else int(rotary_dim)
     max_pos = cos_sin.shape[0] if cos_sin is not None else 0
     cs = _dev(cos_sin, "cos_sin", torch.float32) if cos_sin is not None else None
+    qr = kr = None
+    cp = sp = qrp = krp = None
     if q is not None:
         if q.dim() != 3 or q.shape[0] != T or q.shape[2] != D or q.dtype != k.dtype:
             raise ValueError("q must be [T, Hq, head_dim] of k's dtype")
         Hq = q.shape[1]
-        codes = torch.empty(q.shape, dtype=torch.int8, device=k.device)
-        scales = torch.empty(q.shape[:2], dtype=torch.float32, device=k.device)
-        qp, cp, sp = _dev(q, "q"), codes.data_ptr(), scales.data_ptr()
+        qp = _dev(q, "q")
+        if rotated_bf16:
+            qr = torch.empty(q.shape, dtype=torch.bfloat16, device=k.device)
+            kr = torch.empty(k.shape, dtype=torch.bfloat16, device=k.device)
+            qrp, krp = qr.data_ptr(), kr.data_ptr()
+        else:
+            codes = torch.empty(q.shape, dtype=torch.int8, device=k.device)
+            scales = torch.empty(q.shape[:2], dtype=torch.float32, device=k.device)
+            cp, sp = codes.data_ptr(), scales.data_ptr()
     else:
-        Hq, qp, cp, sp = 6 * H, None, None, None
+        Hq, qp = 6 * H, None
     _check(lib().kv_produce(qp, _dev(k, "k"), _dev(v, "v"), dt, T, Hq, H, D,
                             _dev(positions, "positions", torch.int32), cs, rd, max_pos,
                             _dev(slot_mapping, "slot_mapping", torch.int32), *cache.ptrs(),
-                            cache.num_pages, cp, sp, _stream(stream)))
-    return (codes, scales) if q is not None else None
+                            cache.num_pages, cp, sp, qrp, krp, _stream(stream)))
+    if q is None:
+        return None
+    return (qr, kr) if rotated_bf16 else (codes, scales)
+
+
+def attn_chunk_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+                    sm_scale: float | None = None, out: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """High-precision attention of a chunk over its own bf16 rows: q [n, Hq, 256],
+    k/v [n, Hkv, 256] -> out fp32 [n, Hq, 256]."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16 or t.dim() != 3:
+            raise TypeError(f"{nm} must be bfloat16 [n, heads, head_dim]")
+    n, Hq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != n:
+        raise ValueError("k and v must be [n, Hkv, head_dim]")
+    if out is None:
+        out = torch.empty((n, Hq, D), dtype=torch.float32, device=q.device)
+    sm = float(sm_scale if sm_scale is not None else D ** -0.5)
+    _check(lib().attn_chunk_bf16(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), n, int(bool(causal)),
+                                 Hq, k.shape[1], D, sm, _dev(out, "out", torch.float32),
+                                 _stream(stream)))
+    return out
+
+
+def prefill_step_workspace_bytes(n_new: int, n_q_heads: int, n_kv_heads: int,
+                                 head_dim: int = HEAD_DIM) -> int:
+    return int(lib().prefill_step_workspace_bytes(n_new, n_q_heads, n_kv_heads, head_dim))
+
+
+def prefill_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
+                 cos_sin: torch.Tensor, slot_mapping: torch.Tensor, cache,
+                 block_table: torch.Tensor, context_len: int, sm_scale: float | None = None,
+                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """One prefill chunk end to end (producer, then the route by history): q/k/v bf16 as
+    projected [n_new, heads, 256] -> out fp32 [n_new, Hq, 256]."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16 or t.dim() != 3:
+            raise TypeError(f"{nm} must be bfloat16 [n_new, heads, head_dim]")
+    n_new, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((n_new, Hq, D), dtype=torch.float32, device=q.device)
+    need = prefill_step_workspace_bytes(n_new, Hq, cache.n_kv_heads, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    sm = float(sm_scale if sm_scale is not None else D ** -0.5)
+    _check(lib().prefill_step(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), n_new,
+                              _dev(positions, "positions", torch.int32),
+                              _dev(cos_sin, "cos_sin", torch.float32), cos_sin.shape[1],
+                              cos_sin.shape[0], _dev(slot_mapping, "slot_mapping", torch.int32),
+                              *cache.ptrs(), cache.num_pages,
+                              _dev(block_table, "block_table", torch.int32), int(context_len),
+                              Hq, cache.n_kv_heads, D, sm, _dev(out, "out", torch.float32),
+                              _dev(workspace, "workspace"),
+                              workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
 
 
 def _query(q: torch.Tensor, q_scales, dims: int, what: str):

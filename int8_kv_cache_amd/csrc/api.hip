@@ -102,7 +102,8 @@ int kv_produce(const void* q, const void* k, const void* v, int in_dtype, int n_
                int n_q_heads, int n_kv_heads, int head_dim, const int32_t* positions,
                const float* cos_sin, int rotary_dim, int max_position,
                const int32_t* slot_mapping, int8_t* k_cache, int8_t* v_cache, float* k_scale,
-               float* v_scale, int num_pages, int8_t* q_codes, float* q_scales, void* stream) {
+               float* v_scale, int num_pages, int8_t* q_codes, float* q_scales, uint16_t* q_rot,
+               uint16_t* k_rot, void* stream) {
   if (in_dtype != I8A_DTYPE_F32 && in_dtype != I8A_DTYPE_BF16)
     return set_error(I8A_EINVAL, "kv_produce: in_dtype %d", in_dtype);
   int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
@@ -113,8 +114,9 @@ int kv_produce(const void* q, const void* k, const void* v, int in_dtype, int n_
     return set_error(I8A_EINVAL, "kv_produce: rotary_dim %d (0..256, a multiple of 8)", rotary_dim);
   if (rotary_dim > 0 && (max_position <= 0 || !cos_sin || !positions))
     return set_error(I8A_EINVAL, "kv_produce: RoPE needs positions, cos_sin and max_position > 0");
-  if ((q_codes == nullptr) != (q_scales == nullptr) || (q_codes != nullptr && q == nullptr))
-    return set_error(I8A_EINVAL, "kv_produce: q, q_codes and q_scales go together");
+  if ((q_codes == nullptr) != (q_scales == nullptr) ||
+      ((q_codes != nullptr || q_rot != nullptr) != (q != nullptr)))
+    return set_error(I8A_EINVAL, "kv_produce: q goes with q_codes + q_scales and/or q_rot");
   if (n_tokens == 0) return I8A_OK;
   if (!k || !v || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
     return set_error(I8A_EINVAL, "kv_produce: null pointer");
@@ -123,7 +125,70 @@ int kv_produce(const void* q, const void* k, const void* v, int in_dtype, int n_
   return launch_kv_produce(q, k, v, in_dtype == I8A_DTYPE_BF16, n_tokens, n_q_heads, n_kv_heads,
                            positions, cos_sin, rotary_dim, max_position > 0 ? max_position : 1,
                            slot_mapping, k_cache, v_cache, k_scale, v_scale, num_pages, q_codes,
-                           q_scales, (hipStream_t)stream);
+                           q_scales, q_rot, k_rot, (hipStream_t)stream);
+}
+
+int attn_chunk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n, int causal,
+                    int n_q_heads, int n_kv_heads, int head_dim, float sm_scale, float* out,
+                    void* stream) {
+  int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
+  if (rc) return rc;
+  if (n < 0 || (causal != 0 && causal != 1) || (long long)n * n_q_heads > 2147483000LL)
+    return set_error(I8A_EINVAL, "attn_chunk_bf16: n %d, causal %d", n, causal);
+  if (!isfinite(sm_scale)) return set_error(I8A_EINVAL, "attn_chunk_bf16: sm_scale not finite");
+  if (n == 0) return I8A_OK;
+  if (!q || !k || !v || !out) return set_error(I8A_EINVAL, "attn_chunk_bf16: null pointer");
+  return launch_chunk_bf16(q, k, v, n, causal, n_q_heads, n_kv_heads, sm_scale, out,
+                           (hipStream_t)stream);
+}
+
+size_t prefill_step_workspace_bytes(int n_new, int n_q_heads, int n_kv_heads, int head_dim) {
+  if (n_new <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim != 256) return 0;
+  const size_t rot = (size_t)n_new * (n_q_heads + n_kv_heads) * head_dim * 2;  // bf16 Q, K
+  const size_t q8 = (size_t)n_new * n_q_heads * (head_dim + 4);               // codes + scales
+  const size_t need = rot > q8 ? rot : q8;
+  return (need + 255) / 256 * 256;
+}
+
+int prefill_step(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n_new,
+                 const int32_t* positions, const float* cos_sin, int rotary_dim, int max_position,
+                 const int32_t* slot_mapping, int8_t* k_cache, int8_t* v_cache, float* k_scale,
+                 float* v_scale, int num_pages, const int32_t* block_table, int context_len,
+                 int n_q_heads, int n_kv_heads, int head_dim, float sm_scale, float* out,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
+  if (rc) return rc;
+  if (n_new < 0 || context_len < n_new || context_len < 1)
+    return set_error(I8A_EINVAL, "prefill_step: n_new %d, context_len %d", n_new, context_len);
+  if (n_new == 0) return I8A_OK;
+  if (!workspace || ((uintptr_t)workspace & 255u) != 0)
+    return set_error(I8A_EINVAL, "prefill_step: workspace null or not 256-byte aligned");
+  const size_t need = prefill_step_workspace_bytes(n_new, n_q_heads, n_kv_heads, head_dim);
+  if (workspace_bytes < need)
+    return set_error(I8A_EWORKSPACE, "prefill_step: workspace %zu bytes < %zu needed", workspace_bytes, need);
+  char* ws = static_cast<char*>(workspace);
+  if (context_len == n_new) {
+    // No history: high-precision attention over the chunk's rotated bf16 rows; the
+    // producer still writes the int8 K/V for the later chunks and the decode.
+    uint16_t* q_rot = reinterpret_cast<uint16_t*>(ws);
+    uint16_t* k_rot = q_rot + (size_t)n_new * n_q_heads * head_dim;
+    rc = kv_produce(q, k, v, I8A_DTYPE_BF16, n_new, n_q_heads, n_kv_heads, head_dim, positions,
+                    cos_sin, rotary_dim, max_position, slot_mapping, k_cache, v_cache, k_scale,
+                    v_scale, num_pages, nullptr, nullptr, q_rot, k_rot, stream);
+    if (rc) return rc;
+    return attn_chunk_bf16(q_rot, k_rot, v, n_new, 1, n_q_heads, n_kv_heads, head_dim, sm_scale,
+                           out, stream);
+  }
+  // A history exists (in the int8 cache only): the int8 chunk path with the producer's Q.
+  int8_t* q_codes = reinterpret_cast<int8_t*>(ws);
+  float* q_scales = reinterpret_cast<float*>(ws + (size_t)n_new * n_q_heads * head_dim);
+  rc = kv_produce(q, k, v, I8A_DTYPE_BF16, n_new, n_q_heads, n_kv_heads, head_dim, positions,
+                  cos_sin, rotary_dim, max_position, slot_mapping, k_cache, v_cache, k_scale,
+                  v_scale, num_pages, q_codes, q_scales, nullptr, nullptr, stream);
+  if (rc) return rc;
+  return attn_prefill_chunk_q8(q_codes, q_scales, n_new, k_cache, v_cache, k_scale, v_scale,
+                               block_table, context_len, 1, num_pages, n_q_heads, n_kv_heads,
+                               head_dim, sm_scale, out, stream);
 }
 
 int q_quant(const uint16_t* q_bf16, int n_rows, int head_dim, int8_t* codes, float* scales,

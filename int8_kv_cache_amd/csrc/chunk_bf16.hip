@@ -1,0 +1,272 @@
+// High-precision attention of a prefill chunk with no history, over its own bf16 rows.
+//
+// ("INT8 KV and INT8 MMAC attention on a gfx936 DCU" §3.1: the first prefill chunk has
+// no KV history to read, so it keeps a high-precision attention while the fused producer
+// writes its K/V as int8 for the later chunks and the decode; §3.2: from the point where
+// a history exists the chunk runs the int8 path.)
+//
+// Workgroup = (32 query tokens, KV head g): 12 waves = the 6 query heads of the group x
+// two 16-token halves, every K/V byte staged once in LDS for 192 query rows. Per 64-key
+// block (double buffered; the next block's K moves by direct global->LDS loads and its V
+// through registers while the current one is computed):
+//  * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (exact bf16 products, fp32 sums): tile t
+//    holds keys 16t..16t+15 of the block; the query operands stay in registers;
+//  * online softmax in the exp2 domain with the lazy rescale (the reference max moves
+//    only when a block max exceeds it by more than 2^8);
+//  * out^T += V^T . P^T on v_mfma_f32_16x16x32_bf16 with P carried as two bf16 terms,
+//    hi = bf16(p) and lo = bf16(p - hi) (16 significant bits), and fp32 accumulation, so
+//    the weighted sum keeps fp32-class precision. The 32 keys of one product are the 4
+//    consecutive keys that each lane already holds from two tiles (key index 8 kg + j =
+//    key 16(2h + j/4) + 4 kg + j%4), so P needs no lane movement; V is staged transposed
+//    ([dim][key], padded rows) and read as two 8-byte runs per operand.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace i8a {
+
+namespace {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kCbTok = 32;                  // query tokens per workgroup
+constexpr int kCbWaves = 2 * kGroup;        // (head, 16-token half) per wave
+constexpr int kCbThreads = kCbWaves * 64;   // 768
+constexpr int kVtStride = 64 * 2 + 16;      // bytes per staged V^T row (64 keys + pad)
+constexpr int kKBytes = 32 * 64 * 16;       // staged K block: [dim chunk of 8][key][8 dims]
+constexpr int kVBytes = kHeadDim * kVtStride;
+constexpr float kLazyRescale = 8.0f;
+
+__device__ __forceinline__ uint32_t bf16_rne(float x) {  // finite x
+  const uint32_t b = __float_as_uint(x);
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
+struct Block {
+  int8_t* k;   // staged K block (kKBytes)
+  int8_t* vt;  // staged V^T block (kVBytes)
+};
+
+// Loads of key block kb: K by direct-to-LDS dword x4 loads (instruction c = dim chunk
+// c of 8 dims, lane = key), V into registers (wave w: dim chunks w, w + 12, w + 24 of
+// key = lane); keys past the chunk re-read the last one (they are masked).
+struct Loader {
+  const uint16_t* k;
+  const uint16_t* v;
+  int n, n_kv_heads, g, w, lane;
+
+  __device__ __forceinline__ size_t row(int kb) const {
+    const int key = min(kb * 64 + lane, n - 1);
+    return ((size_t)key * n_kv_heads + g) * kHeadDim;
+  }
+  __device__ __forceinline__ void issue_k(int kb, int8_t* k_lds) const {
+    const size_t r = row(kb);
+    for (int c = w; c < 32; c += kCbWaves)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(k + r + c * 8),
+          (__attribute__((address_space(3))) void*)(k_lds + c * 1024), 16, 0, 0);
+  }
+  __device__ __forceinline__ void load_v(int kb, uint4* vr) const {
+    const size_t r = row(kb);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int c = w + kCbWaves * i;
+      if (c < 32) vr[i] = *reinterpret_cast<const uint4*>(v + r + c * 8);
+    }
+  }
+  // Transposed store: dim 8c + j of key `lane` -> V^T row 8c + j, column lane.
+  __device__ __forceinline__ void store_vt(const uint4* vr, int8_t* vt) const {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int c = w + kCbWaves * i;
+      if (c < 32) {
+        const uint32_t d[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint16_t e = (uint16_t)(d[j >> 1] >> (16 * (j & 1)));
+          *reinterpret_cast<uint16_t*>(vt + (8 * c + j) * kVtStride + lane * 2) = e;
+        }
+      }
+    }
+  }
+};
+
+struct RowState {
+  float m_run, l_part;
+  v4f acc[16];
+};
+
+// One 64-key block: QK, softmax, PV from the staged block `cur`; the loads of block kb+1
+// (K into `nxt`, V into registers) go out first, and their V lands in `nxt` at the end.
+__device__ __forceinline__ void block_step(int kb, int nkb, const Loader& ld, const v8bf* qop,
+                                           int my_tok, bool causal, int n, float qk_scale_log2,
+                                           int gq, int nn, RowState& st, Block cur, Block nxt) {
+  uint4 vr[3];
+  const bool more = kb + 1 < nkb;
+  if (more) {
+    ld.issue_k(kb + 1, nxt.k);
+    ld.load_v(kb + 1, vr);
+  }
+  // S^T tile t: rows = keys 16t..16t+15 (lane (m, kg) reads key 16t + m, dims 32u + 8kg..)
+  v4f S[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    S[t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const v8bf a = *reinterpret_cast<const v8bf*>(cur.k + (4 * u + gq) * 1024 + (16 * t + nn) * 16);
+      S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[u], S[t], 0, 0, 0);
+    }
+  }
+  // Lane (nn, gq) holds keys 64kb + 16t + 4gq + i of its query row.
+  const int key0 = kb * 64;
+  float x[16];
+  float bmax = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = key0 + 16 * t + 4 * gq + i;
+      const bool vis = key < n && (!causal || key <= my_tok);
+      x[4 * t + i] = vis ? S[t][i] * qk_scale_log2 : -INFINITY;
+      bmax = fmaxf(bmax, x[4 * t + i]);
+    }
+  bmax = col_max(bmax);
+  if (__any(bmax > st.m_run + kLazyRescale)) {
+    const float m_new = fmaxf(st.m_run, bmax);
+    const float alpha = m_new == st.m_run ? 1.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) st.acc[dt] *= alpha;
+    st.l_part *= alpha;
+    st.m_run = m_new;
+  }
+  const float mu = st.m_run == -INFINITY ? 0.f : st.m_run;
+  // B operands of the two 32-key halves: h holds tiles 2h and 2h + 1 (elements 8h..8h+7).
+  uint4 ph[2], pl[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int j2 = 0; j2 < 4; ++j2) {
+      uint32_t hb[2], lb[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const float p = __builtin_amdgcn_exp2f(x[8 * h + 2 * j2 + b] - mu);
+        st.l_part += p;
+        hb[b] = bf16_rne(p);
+        lb[b] = bf16_rne(p - __uint_as_float(hb[b] << 16));
+      }
+      hw[j2] = hb[0] | (hb[1] << 16);
+      lw[j2] = lb[0] | (lb[1] << 16);
+    }
+    ph[h] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    pl[h] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  }
+  // out^T(dt) += V^T(dt) . P^T: lane (nn, gq) reads dim 16dt + nn, keys 32h + 4gq..+3 and
+  // 32h + 16 + 4gq..+3 (tiles 2h and 2h + 1).
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) {
+    const int8_t* vrow = cur.vt + (16 * dt + nn) * kVtStride + 8 * gq;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint2 a0 = *reinterpret_cast<const uint2*>(vrow + 64 * h);
+      const uint2 a1 = *reinterpret_cast<const uint2*>(vrow + 64 * h + 32);
+      const v8bf a = __builtin_bit_cast(v8bf, make_uint4(a0.x, a0.y, a1.x, a1.y));
+      st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, ph[h]),
+                                                           st.acc[dt], 0, 0, 0);
+      st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, pl[h]),
+                                                           st.acc[dt], 0, 0, 0);
+    }
+  }
+  if (more) {
+    ld.store_vt(vr, nxt.vt);
+    __builtin_amdgcn_s_waitcnt(0);  // the next K block has landed in LDS
+  }
+  lds_barrier();
+}
+
+__global__ __launch_bounds__(kCbThreads, 1) void chunk_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int n, int causal, int n_q_heads, int n_kv_heads,
+    float qk_scale_log2, float* __restrict__ out, int n_qb, int xcd_per_head) {
+  int qb, g;
+  {  // XCD-aware order as in the int8 chunk kernel: each KV head on its own XCDs
+    const int L = blockIdx.x, xcd = L % 8, slot = L / 8;
+    if (xcd_per_head > 0) {
+      g = xcd / xcd_per_head;
+      qb = slot * xcd_per_head + xcd % xcd_per_head;
+    } else {
+      g = L / n_qb;
+      qb = L % n_qb;
+    }
+    if (qb >= n_qb || g >= n_kv_heads) return;  // padding workgroup (whole block)
+  }
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = w >> 1, half = w & 1;
+  const int h = g * kGroup + hl;
+  const int nn = lane & 15, gq = lane >> 4;
+  const int t0 = qb * kCbTok;
+  const int my_tok = t0 + 16 * half + nn;
+  const int last_tok = min(t0 + kCbTok, n) - 1;
+  const int kend = causal ? last_tok + 1 : n;
+  const int nkb = (kend + 63) >> 6;
+
+  __shared__ __align__(16) int8_t s_k0[kKBytes];
+  __shared__ __align__(16) int8_t s_k1[kKBytes];
+  __shared__ __align__(16) int8_t s_v0[kVBytes];
+  __shared__ __align__(16) int8_t s_v1[kVBytes];
+
+  const Loader ld{k, v, n, n_kv_heads, g, w, lane};
+  {
+    uint4 vr[3];
+    ld.issue_k(0, s_k0);
+    ld.load_v(0, vr);
+    // Query operands: lane (nn, gq) holds dims 32u + 8gq..+7 of its row (rows past the
+    // chunk re-read the last one; their outputs are not stored).
+    v8bf qop[8];
+    const size_t qrow = ((size_t)min(my_tok, n - 1) * n_q_heads + h) * kHeadDim;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) qop[u] = *reinterpret_cast<const v8bf*>(q + qrow + 32 * u + 8 * gq);
+    ld.store_vt(vr, s_v0);
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+
+    RowState st;
+    st.m_run = -INFINITY;
+    st.l_part = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) st.acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+    const Block b0{s_k0, s_v0}, b1{s_k1, s_v1};
+    for (int kb = 0; kb < nkb; kb += 2) {
+      block_step(kb, nkb, ld, qop, my_tok, causal != 0, n, qk_scale_log2, gq, nn, st, b0, b1);
+      if (kb + 1 < nkb)
+        block_step(kb + 1, nkb, ld, qop, my_tok, causal != 0, n, qk_scale_log2, gq, nn, st, b1, b0);
+    }
+    const float l = col_sum(st.l_part);
+    if (my_tok < n) {
+      const float il = 1.0f / l;
+      float* o = out + ((size_t)my_tok * n_q_heads + h) * kHeadDim + 4 * gq;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt)
+        *reinterpret_cast<float4*>(o + 16 * dt) =
+            make_float4(st.acc[dt][0] * il, st.acc[dt][1] * il, st.acc[dt][2] * il, st.acc[dt][3] * il);
+    }
+  }
+}
+
+}  // namespace
+
+int launch_chunk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n, int causal,
+                      int n_q_heads, int n_kv_heads, float sm_scale, float* out,
+                      hipStream_t stream) {
+  const int n_qb = (n + kCbTok - 1) / kCbTok;
+  const int xcd_per_head = (n_kv_heads <= 8 && 8 % n_kv_heads == 0) ? 8 / n_kv_heads : 0;
+  const long long n_wg = xcd_per_head > 0 ? 8LL * ((n_qb + xcd_per_head - 1) / xcd_per_head)
+                                          : (long long)n_qb * n_kv_heads;
+  hipLaunchKernelGGL(chunk_bf16_kernel, dim3((unsigned)n_wg), dim3(kCbThreads), 0, stream, q, k,
+                     v, n, causal, n_q_heads, n_kv_heads, sm_scale * kLog2e, out, n_qb,
+                     xcd_per_head);
+  return check_launch("attn_chunk_bf16");
+}
+
+}  // namespace i8a

@@ -18,7 +18,11 @@ int launch_kv_produce(const void* q, const void* k, const void* v, int in_bf16, 
                       int n_q_heads, int n_kv_heads, const int32_t* positions, const float* cos_sin,
                       int rotary_dim, int max_pos, const int32_t* slots, int8_t* k_cache,
                       int8_t* v_cache, float* k_scale, float* v_scale, int num_pages,
-                      int8_t* q_codes, float* q_scales, hipStream_t stream);
+                      int8_t* q_codes, float* q_scales, uint16_t* q_rot, uint16_t* k_rot,
+                      hipStream_t stream);
+int launch_chunk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n, int causal,
+                      int n_q_heads, int n_kv_heads, float sm_scale, float* out,
+                      hipStream_t stream);
 int launch_q_quant(const uint16_t* q, int n_rows, int8_t* codes, float* scales,
                    hipStream_t stream);
 // q: bf16 rows to quantize (q_scales == nullptr) or int8 codes with q_scales (kv_produce).

@@ -71,7 +71,18 @@ struct Produce {
   int rotary_dim, max_pos, n_q_heads;
   int8_t* q_codes;
   float* q_scales;
+  uint16_t* q_rot;  // rotated Q / K rows rounded to bf16 (a chunk with no history)
+  uint16_t* k_rot;
 };
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) {  // nearest, ties to even; finite x
+  const uint32_t b = __float_as_uint(x);
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, const float* x) {
+  *reinterpret_cast<uint2*>(dst) = make_uint2(bf16_bits(x[0]) | (bf16_bits(x[1]) << 16),
+                                              bf16_bits(x[2]) | (bf16_bits(x[3]) << 16));
+}
 
 template <int IN_BF16, int PRODUCE>
 __global__ __launch_bounds__(256) void kv_quant_write_kernel(
@@ -108,7 +119,7 @@ __global__ __launch_bounds__(256) void kv_quant_write_kernel(
   // Query rows of the group for this wave's tokens, loaded with the K/V rows (one round
   // trip); tokens past the batch re-read the last one and are not stored.
   float qx[PRODUCE ? 4 : 1][kGroup][4];
-  const bool want_q = PRODUCE && pr.q_codes != nullptr;
+  const bool want_q = PRODUCE && (pr.q_codes != nullptr || pr.q_rot != nullptr);
   if (want_q) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -129,6 +140,13 @@ __global__ __launch_bounds__(256) void kv_quant_write_kernel(
       rope4(kx[i], cs_row[i], pr.rotary_dim, lane);
     }
   }
+  if (PRODUCE && pr.k_rot != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = tok0 + 4 * w + i;
+      if (t < n_tokens) store_bf16x4(pr.k_rot + ((size_t)t * n_kv_heads + head) * kHeadDim + lane * 4, kx[i]);
+    }
+  }
   uint32_t kq[4], vq[4];
   float ks[4], vs[4];
 #pragma unroll
@@ -146,11 +164,14 @@ __global__ __launch_bounds__(256) void kv_quant_write_kernel(
       for (int hh = 0; hh < kGroup; ++hh) {
         float* xr = qx[PRODUCE ? i : 0][hh];
         if (pr.rotary_dim > 0) rope4(xr, cs_row[i], pr.rotary_dim, lane);
-        float sc;
-        const uint32_t c = quantize4(xr[0], xr[1], xr[2], xr[3], &sc);
         const size_t row = (size_t)t * pr.n_q_heads + head * kGroup + hh;
-        *reinterpret_cast<uint32_t*>(pr.q_codes + row * kHeadDim + lane * 4) = c;
-        if (lane == 0) pr.q_scales[row] = sc;
+        if (pr.q_rot != nullptr) store_bf16x4(pr.q_rot + row * kHeadDim + lane * 4, xr);
+        if (pr.q_codes != nullptr) {
+          float sc;
+          const uint32_t c = quantize4(xr[0], xr[1], xr[2], xr[3], &sc);
+          *reinterpret_cast<uint32_t*>(pr.q_codes + row * kHeadDim + lane * 4) = c;
+          if (lane == 0) pr.q_scales[row] = sc;
+        }
       }
     }
   }
@@ -224,7 +245,7 @@ int launch_kv_quant_write(const void* k, const void* v, int in_bf16, int n_token
                           float* v_scale, int num_pages, hipStream_t stream) {
   const dim3 grid((n_tokens + 15) / 16, n_kv_heads), block(256);
   const long long n_slots = (long long)num_pages * kPage;
-  const Produce none{nullptr, nullptr, nullptr, 0, 1, 0, nullptr, nullptr};
+  const Produce none{nullptr, nullptr, nullptr, 0, 1, 0, nullptr, nullptr, nullptr, nullptr};
   if (in_bf16)
     hipLaunchKernelGGL((kv_quant_write_kernel<1, 0>), grid, block, 0, stream, k, v, n_tokens,
                        n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots, none);
@@ -238,10 +259,12 @@ int launch_kv_produce(const void* q, const void* k, const void* v, int in_bf16, 
                       int n_q_heads, int n_kv_heads, const int32_t* positions, const float* cos_sin,
                       int rotary_dim, int max_pos, const int32_t* slots, int8_t* k_cache,
                       int8_t* v_cache, float* k_scale, float* v_scale, int num_pages,
-                      int8_t* q_codes, float* q_scales, hipStream_t stream) {
+                      int8_t* q_codes, float* q_scales, uint16_t* q_rot, uint16_t* k_rot,
+                      hipStream_t stream) {
   const dim3 grid((n_tokens + 15) / 16, n_kv_heads), block(256);
   const long long n_slots = (long long)num_pages * kPage;
-  const Produce pr{q, positions, cos_sin, rotary_dim, max_pos, n_q_heads, q_codes, q_scales};
+  const Produce pr{q, positions, cos_sin, rotary_dim, max_pos, n_q_heads, q_codes, q_scales,
+                   q_rot, k_rot};
   if (in_bf16)
     hipLaunchKernelGGL((kv_quant_write_kernel<1, 1>), grid, block, 0, stream, k, v, n_tokens,
                        n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots, pr);

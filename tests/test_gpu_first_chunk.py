@@ -1,0 +1,110 @@
+"""The high-precision route of a chunk with no history ("INT8 KV and INT8 MMAC attention
+on a gfx936 DCU" §3.1, §3.2): attn_chunk_bf16 against exact attention on the same bf16
+rows (max abs error <= 1e-4 * max|V|, the fp32-class bar), the producer's rotated bf16
+rows bit for bit, and prefill_step's routing: no history -> bf16 attention on the rotated
+rows, a history -> the int8 chunk path on the producer's Q codes."""
+import numpy as np
+import pytest
+import torch
+
+import int8_kv_cache_amd as lib
+import workloads
+from oracle import attention, paged, quant, rope
+from tests.gpu_support import cache_to_host, gpu_cache, need_gpu, oracle_cache, say, up
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def _bf16(bits):
+    return up(bits.view(np.int16)).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("n,causal", [(1, True), (33, True), (64, True), (300, True),
+                                      (300, False), (2048, True)])
+def test_chunk_bf16_matches_exact(n, causal):
+    need_gpu()
+    say(f"attn_chunk_bf16 n={n} causal={causal}")
+    rng = np.random.default_rng(200 + n)
+    q = rng.standard_normal((n, 24, 256), dtype=np.float32)
+    k = rng.standard_normal((n, 4, 256), dtype=np.float32)
+    k[:, :, rng.choice(256, 4, replace=False)] *= np.float32(10.0)
+    v = rng.standard_normal((n, 4, 256), dtype=np.float32)
+    qb, kb, vb = (workloads.f32_to_bf16_bits(a) for a in (q, k, v))
+    out = lib.attn_chunk_bf16(_bf16(qb), _bf16(kb), _bf16(vb), causal=causal)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    qd, kd, vd = (quant.bf16_bits_to_f32(a).astype(np.float64) for a in (qb, kb, vb))
+    rows = np.arange(n) if n <= 300 else np.array([0, 1, 63, 64, 65, 500, 1023, 1024, 2047])
+    last = rows if causal else np.full(rows.shape, n - 1)
+    ref = attention.attention_exact(qd[rows], kd, vd, 1 / 16, last)
+    vmax = float(np.max(np.abs(vd)))
+    err = float(np.max(np.abs(o[rows] - ref)))
+    say(f"  err {err:.3e} (bound {TOL * vmax:.3e})")
+    assert err <= TOL * vmax
+
+
+def test_producer_rotated_rows_bit_exact():
+    need_gpu()
+    case = workloads.make_producer_case(210, 300, start=0, rotary_dim=128)
+    q, k, v = case.data()
+    qb, kb, vb = (workloads.f32_to_bf16_bits(a) for a in (q, k, v))
+    q, k, v = (quant.bf16_bits_to_f32(a) for a in (qb, kb, vb))
+    table = case.table()
+    say("kv_produce with rotated bf16 outputs (300 tokens, rotary_dim 128)")
+    cache = gpu_cache(case.num_pages, 4)
+    qr, kr = lib.kv_produce(_bf16(qb), _bf16(kb), _bf16(vb), up(case.positions), up(table),
+                            up(case.slots), cache, rotated_bf16=True)
+    torch.cuda.synchronize()
+    ref_cache = oracle_cache(case.num_pages, 4)
+    rq, rk = rope.produce_first_chunk(q, k, v, case.positions, table, 128, case.slots, ref_cache)
+    assert np.array_equal(qr.cpu().view(torch.int16).numpy().view(np.uint16), rq)
+    assert np.array_equal(kr.cpu().view(torch.int16).numpy().view(np.uint16), rk)
+    for a, b in zip(cache_to_host(cache), ref_cache):
+        assert np.array_equal(a, b)
+
+
+def test_prefill_step_routes_by_history():
+    need_gpu()
+    say("prefill_step: 300-token first chunk (bf16 route), then 100 tokens (int8 route)")
+    full = workloads.make_producer_case(220, 400, start=0, rotary_dim=256)
+    q, k, v = full.data()
+    qb, kb, vb = (workloads.f32_to_bf16_bits(a) for a in (q, k, v))
+    q, k, v = (quant.bf16_bits_to_f32(a) for a in (qb, kb, vb))
+    table = full.table()
+    cache = gpu_cache(full.num_pages, 4)
+    block_row = up((full.slots[::16] // 16).astype(np.int32))
+    outs = []
+    for a, b in ((0, 300), (300, 400)):
+        sl = slice(a, b)
+        outs.append(lib.prefill_step(_bf16(qb[sl]), _bf16(kb[sl]), _bf16(vb[sl]),
+                                     up(full.positions[sl]), up(table), up(full.slots[sl]), cache,
+                                     block_row, b))
+    torch.cuda.synchronize()
+    ref_cache = oracle_cache(full.num_pages, 4)
+    rq, rk = rope.produce_first_chunk(q[:300], k[:300], v[:300], full.positions[:300], table, 256,
+                                      full.slots[:300], ref_cache)
+    # first chunk: exact attention on the rotated bf16 rows and the input V
+    qd, kd = quant.bf16_bits_to_f32(rq).astype(np.float64), quant.bf16_bits_to_f32(rk).astype(np.float64)
+    ref1 = attention.attention_exact(qd, kd, v[:300].astype(np.float64), 1 / 16, np.arange(300))
+    vmax = float(np.max(np.abs(v)))
+    e1 = float(np.max(np.abs(outs[0].cpu().numpy() - ref1)))
+    say(f"  first chunk: err {e1:.3e} (bound {TOL * vmax:.3e})")
+    assert e1 <= TOL * vmax
+    # second chunk: the int8 path over the whole int8 cache with the producer's Q codes
+    qc, qs = rope.produce(q[300:], k[300:], v[300:], full.positions[300:], table, 256,
+                          full.slots[300:], ref_cache)
+    for a_, b_ in zip(cache_to_host(cache), ref_cache):
+        assert np.array_equal(a_, b_)
+    view = paged.gather_seq(ref_cache, full.slots[::16] // 16, 400, 4)
+    kc, ks, vc, vs = view
+    qd2 = quant.dequantize(qc, qs)
+    last = 300 + np.arange(100)
+    ref_a = attention.attention_exact(qd2, quant.dequantize(kc, ks), quant.dequantize(vc, vs), 1 / 16, last)
+    ref_b = attention.attention_int8p(qd2, quant.dequantize(kc, ks), vc, vs, 1 / 16, last)
+    vmax2 = float(np.max(np.abs(quant.dequantize(vc, vs))))
+    o2 = outs[1].cpu().numpy()
+    ea, eb = float(np.max(np.abs(o2 - ref_a))), float(np.max(np.abs(o2 - ref_b)))
+    say(f"  second chunk: err vs exact {ea:.3e}, vs int8-P rule {eb:.3e} (max|V| {vmax2:.3f})")
+    assert ea <= 1e-2 * vmax2 and eb <= 1e-3 * vmax2

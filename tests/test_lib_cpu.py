@@ -176,7 +176,7 @@ def test_kv_produce_and_q8_validation():
     C = _codes()
     L = m.lib()
     base = [FAKE, FAKE, FAKE, 1, 4, 24, 4, 256, FAKE, FAKE, 64, 100, FAKE, FAKE, FAKE, FAKE, FAKE,
-            10, FAKE, FAKE, None]
+            10, FAKE, FAKE, None, None, None]
 
     def call(i=None, val=None):
         a = list(base)
@@ -192,6 +192,14 @@ def test_kv_produce_and_q8_validation():
     assert call(5, 12) == C["I8A_EUNSUPPORTED"]         # group of 3
     assert call(3, 7) == C["I8A_EINVAL"]                # dtype
     assert call(4, 0) == C["I8A_OK"]                    # no tokens
+    assert call(0, None) == C["I8A_EINVAL"]             # q_codes without q
+    cb = [FAKE, FAKE, FAKE, 64, 2, 24, 4, 256, 0.0625, FAKE, None]
+    assert L.attn_chunk_bf16(*cb) == C["I8A_EINVAL"]    # causal flag
+    ps = m.prefill_step_workspace_bytes(100, 24, 4)
+    assert ps == (100 * 28 * 256 * 2 + 255) // 256 * 256
+    step = [FAKE, FAKE, FAKE, 100, FAKE, FAKE, 64, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, 50, FAKE,
+            100, 24, 4, 256, 0.0625, FAKE, 4096, ps - 1, None]
+    assert L.prefill_step(*step) == C["I8A_EWORKSPACE"]
     dec = [FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 100, 10, 24, 4, 256, 0.0625,
            FAKE, FAKE, 1 << 20, None]
     assert L.attn_decode_q8(*dec) == C["I8A_EINVAL"]     # codes without scales
