@@ -116,6 +116,7 @@ struct RowCtx {
   int koff, voff;      // A-operand byte offsets in a staged K / V block
   int gq, lim, kfull, ctx;
   float rs;            // sQ * sm_scale * log2(e), > 0
+  v4i qB[4];           // the query operand, held for the whole loop
 };
 
 // Running softmax state of one lane: its query row's max and partial sum, 64 of the
@@ -133,19 +134,31 @@ __device__ __forceinline__ void block_step(
     int kb, int nkb, const BlockLoader& ld, BlockLoader::Pages& pg_next, const RowCtx& rc,
     RowState& st, const int8_t* sK, const int8_t* sV, const float* sSk, const float* sSv,
     int8_t (*nKV)[4 * kPfPage], float (*nSc)[64]) {
-  // QK: S[t] rows = tokens 4t..4t+3 of each of the 4 pages
+  // QK: S[t] rows = tokens 4t..4t+3 of each of the 4 pages. The operands of group u+1
+  // are read while the products of group u run.
   v4i S[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) S[t] = v4i{0, 0, 0, 0};
+  v4i ka[4], qa;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) ka[t] = *reinterpret_cast<const v4i*>(sK + rc.koff + t * 64);
+  qa = rc.qB[0];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const v4i b = *reinterpret_cast<const v4i*>(rc.qcol + u * 64);
+    v4i kn[4], qn;
+    if (u < 3) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const v4i a = *reinterpret_cast<const v4i*>(sK + rc.koff + u * 1024 + t * 64);
-      S[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, S[t], 0, 0, 0);
+      for (int t = 0; t < 4; ++t) kn[t] = *reinterpret_cast<const v4i*>(sK + rc.koff + (u + 1) * 1024 + t * 64);
+      qn = rc.qB[u + 1];
     }
-    __builtin_amdgcn_sched_barrier(0);  // bound the operand registers in flight
+#pragma unroll
+    for (int t = 0; t < 4; ++t) S[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[t], qa, S[t], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (u < 3) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ka[t] = kn[t];
+      qa = qn;
+    }
   }
   // The next block's loads go out once this block's query reads are issued.
   if (kb + 1 < nkb) {
@@ -213,18 +226,31 @@ __device__ __forceinline__ void block_step(
   }
 
   // PV: out^T(dim tile dt) += s_b * V^T(dt) . P^T; the A operand of lane (n, gq) is
-  // the 16 token codes of dim 16dt + n in page gq, one 16-byte LDS read.
+  // the 16 token codes of dim 16dt + n in page gq, one 16-byte LDS read. The operands of
+  // group q4+1 are read while the products of group q4 run; each group's fold follows
+  // its 4 products.
+  v4i va[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) va[u] = *reinterpret_cast<const v4i*>(sV + rc.voff + u * 256);
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
+    v4i vn[4];
+    if (q4 < 3) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int dt = q4 * 4 + u;
-      const v4i a = *reinterpret_cast<const v4i*>(sV + rc.voff + dt * 256);
-      const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, Pb, kMagic4, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st.acc[dt][i] = fmaf(__int_as_float(r[i]), sb, st.acc[dt][i]);
+      for (int u = 0; u < 4; ++u) vn[u] = *reinterpret_cast<const v4i*>(sV + rc.voff + ((q4 + 1) * 4 + u) * 256);
     }
+    v4i r[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(va[u], Pb, kMagic4, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.acc[q4 * 4 + u][i] = fmaf(__int_as_float(r[u][i]), sb, st.acc[q4 * 4 + u][i]);
     __builtin_amdgcn_sched_barrier(0);
+    if (q4 < 3) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) va[u] = vn[u];
+    }
   }
   st.corr = fmaf(sb, kMagicF, st.corr);
   if ((kb & (kFlushBlocks - 1)) == kFlushBlocks - 1) {  // bounds the offset carried
@@ -232,6 +258,11 @@ __device__ __forceinline__ void block_step(
     for (int dt = 0; dt < 16; ++dt) st.acc[dt] -= st.corr;
     st.corr = 0.f;
   }
+  // Pin the fold and the row sum of this block before the barrier (left alone, the
+  // compiler sinks them past it and keeps the 16 raw products live across).
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) asm volatile("" : "+v"(st.acc[dt]));
+  asm volatile("" : "+v"(st.l_part), "+v"(st.corr));
   if (kb + 1 < nkb) __builtin_amdgcn_s_waitcnt(0);  // the next block has landed in LDS
   lds_barrier();
 }
@@ -329,6 +360,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
   rc.ctx = ctx;
   // rs > 0 keeps max(x) = rs * max(y) and exp2(fma(y, rs, -m)) = 0 for masked y = -inf.
   rc.rs = fmaxf(s_qs[hl][16 * half + n] * qk_scale_log2, 1e-30f);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) rc.qB[u] = *reinterpret_cast<const v4i*>(rc.qcol + u * 64);
 
   RowState st;
   st.m_run = -INFINITY;
