@@ -7,18 +7,20 @@
 //
 // Workgroup = (32 query tokens, KV head g): 12 waves = the 6 query heads of the group x
 // two 16-token halves, every K/V byte staged once in LDS for 192 query rows. Per 64-key
-// block (double buffered; the next block's K moves by direct global->LDS loads and its V
-// through registers while the current one is computed):
+// block (double buffered; the next block's K and V move by direct global->LDS loads while
+// the current one is computed):
 //  * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (exact bf16 products, fp32 sums): tile t
 //    holds keys 16t..16t+15 of the block; the query operands stay in registers;
 //  * online softmax in the exp2 domain with the lazy rescale (the reference max moves
 //    only when a block max exceeds it by more than 2^8);
 //  * out^T += V^T . P^T on v_mfma_f32_16x16x32_bf16 with P carried as two bf16 terms,
-//    hi = bf16(p) and lo = bf16(p - hi) (16 significant bits), and fp32 accumulation, so
+//    hi = bf16(p) and lo = bf16(p - hi) (16 significant bits; gfx950's packed fp32 -> bf16
+//    conversion rounds two values to nearest even per instruction), and fp32 accumulation, so
 //    the weighted sum keeps fp32-class precision. The 32 keys of one product are the 4
 //    consecutive keys that each lane already holds from two tiles (key index 8 kg + j =
-//    key 16(2h + j/4) + 4 kg + j%4), so P needs no lane movement; V is staged transposed
-//    ([dim][key], padded rows) and read as two 8-byte runs per operand.
+//    key 16(2h + j/4) + 4 kg + j%4), so P needs no lane movement; V is staged as key rows
+//    by direct-to-LDS loads and read with gfx950's transposing LDS read (ds_read_b64_tr_b16),
+//    two per operand.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -27,28 +29,24 @@ namespace i8a {
 namespace {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int kCbTok = 32;                  // query tokens per workgroup
 constexpr int kCbWaves = 2 * kGroup;        // (head, 16-token half) per wave
 constexpr int kCbThreads = kCbWaves * 64;   // 768
-constexpr int kVtStride = 64 * 2 + 16;      // bytes per staged V^T row (64 keys + pad)
 constexpr int kKBytes = 32 * 64 * 16;       // staged K block: [dim chunk of 8][key][8 dims]
-constexpr int kVBytes = kHeadDim * kVtStride;
+constexpr int kVBytes = 64 * kHeadDim * 2;   // staged V block: [key][256 dims], swizzled
 constexpr float kLazyRescale = 8.0f;
-
-__device__ __forceinline__ uint32_t bf16_rne(float x) {  // finite x
-  const uint32_t b = __float_as_uint(x);
-  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
-}
 
 struct Block {
   int8_t* k;   // staged K block (kKBytes)
-  int8_t* vt;  // staged V^T block (kVBytes)
+  int8_t* v;   // staged V block (kVBytes)
 };
 
-// Loads of key block kb: K by direct-to-LDS dword x4 loads (instruction c = dim chunk
-// c of 8 dims, lane = key), V into registers (wave w: dim chunks w, w + 12, w + 24 of
-// key = lane); keys past the chunk re-read the last one (they are masked).
+// Loads of key block kb by direct-to-LDS dword x4 loads: K as instruction c = dim chunk
+// c of 8 dims, lane = key; V as key rows. Keys past the chunk re-read the last one (they
+// are masked).
 struct Loader {
   const uint16_t* k;
   const uint16_t* v;
@@ -65,27 +63,19 @@ struct Loader {
           (const __attribute__((address_space(1))) void*)(k + r + c * 8),
           (__attribute__((address_space(3))) void*)(k_lds + c * 1024), 16, 0, 0);
   }
-  __device__ __forceinline__ void load_v(int kb, uint4* vr) const {
-    const size_t r = row(kb);
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int c = w + kCbWaves * i;
-      if (c < 32) vr[i] = *reinterpret_cast<const uint4*>(v + r + c * 8);
-    }
-  }
-  // Transposed store: dim 8c + j of key `lane` -> V^T row 8c + j, column lane.
-  __device__ __forceinline__ void store_vt(const uint4* vr, int8_t* vt) const {
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int c = w + kCbWaves * i;
-      if (c < 32) {
-        const uint32_t d[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint16_t e = (uint16_t)(d[j >> 1] >> (16 * (j & 1)));
-          *reinterpret_cast<uint16_t*>(vt + (8 * c + j) * kVtStride + lane * 2) = e;
-        }
-      }
+  // V rows (512 B per key) by direct-to-LDS dword x4 loads, two keys per instruction
+  // (instruction i = keys 2i, 2i+1). The 16-byte chunks of key row r are stored XOR-ed
+  // with (r & 7) << 1: LDS chunk c of row r holds dims 8 (c ^ ((r & 7) << 1)) .. +7, so
+  // the transposed reads of 16 rows at one dim range spread over all banks.
+  __device__ __forceinline__ void issue_v(int kb, int8_t* v_lds) const {
+    const int half = lane >> 5, c = lane & 31;
+    for (int i = w; i < 32; i += kCbWaves) {
+      const int r = 2 * i + half;
+      const int key = min(kb * 64 + r, n - 1);
+      const size_t src = ((size_t)key * n_kv_heads + g) * kHeadDim + 8 * (c ^ ((r & 7) << 1));
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(v + src),
+                                       (__attribute__((address_space(3))) void*)(v_lds + i * 1024),
+                                       16, 0, 0);
     }
   }
 };
@@ -96,15 +86,16 @@ struct RowState {
 };
 
 // One 64-key block: QK, softmax, PV from the staged block `cur`; the loads of block kb+1
-// (K into `nxt`, V into registers) go out first, and their V lands in `nxt` at the end.
+// into `nxt` go out first.
 __device__ __forceinline__ void block_step(int kb, int nkb, const Loader& ld, const v8bf* qop,
-                                           int my_tok, bool causal, int n, float qk_scale_log2,
-                                           int gq, int nn, RowState& st, Block cur, Block nxt) {
-  uint4 vr[3];
+                                           int my_tok, int first_tok, bool causal, int n,
+                                           float qk_scale_log2,
+                                           int gq, int nn, const int* vaddr, RowState& st,
+                                           Block cur, Block nxt) {
   const bool more = kb + 1 < nkb;
   if (more) {
     ld.issue_k(kb + 1, nxt.k);
-    ld.load_v(kb + 1, vr);
+    ld.issue_v(kb + 1, nxt.v);
   }
   // S^T tile t: rows = keys 16t..16t+15 (lane (m, kg) reads key 16t + m, dims 32u + 8kg..)
   v4f S[4];
@@ -117,19 +108,24 @@ __device__ __forceinline__ void block_step(int kb, int nkb, const Loader& ld, co
       S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[u], S[t], 0, 0, 0);
     }
   }
-  // Lane (nn, gq) holds keys 64kb + 16t + 4gq + i of its query row.
+  // Lane (nn, gq) holds keys 64kb + 16t + 4gq + i of its query row. Only blocks that
+  // reach past the chunk or past the workgroup's first row need the mask.
   const int key0 = kb * 64;
   float x[16];
   float bmax = -INFINITY;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int e = 0; e < 16; ++e) x[e] = S[e >> 2][e & 3] * qk_scale_log2;
+  if (key0 + 64 > n || (causal && key0 + 63 > first_tok)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = key0 + 16 * t + 4 * gq + i;
-      const bool vis = key < n && (!causal || key <= my_tok);
-      x[4 * t + i] = vis ? S[t][i] * qk_scale_log2 : -INFINITY;
-      bmax = fmaxf(bmax, x[4 * t + i]);
-    }
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = key0 + 16 * t + 4 * gq + i;
+        if (!(key < n && (!causal || key <= my_tok))) x[4 * t + i] = -INFINITY;
+      }
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, x[e]);
   bmax = col_max(bmax);
   if (__any(bmax > st.m_run + kLazyRescale)) {
     const float m_new = fmaxf(st.m_run, bmax);
@@ -141,46 +137,48 @@ __device__ __forceinline__ void block_step(int kb, int nkb, const Loader& ld, co
   }
   const float mu = st.m_run == -INFINITY ? 0.f : st.m_run;
   // B operands of the two 32-key halves: h holds tiles 2h and 2h + 1 (elements 8h..8h+7).
+  // hi = bf16(p) and lo = bf16(p - hi), both rounded to nearest even by the hardware
+  // conversion (two values per instruction).
   uint4 ph[2], pl[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     uint32_t hw[4], lw[4];
 #pragma unroll
     for (int j2 = 0; j2 < 4; ++j2) {
-      uint32_t hb[2], lb[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const float p = __builtin_amdgcn_exp2f(x[8 * h + 2 * j2 + b] - mu);
-        st.l_part += p;
-        hb[b] = bf16_rne(p);
-        lb[b] = bf16_rne(p - __uint_as_float(hb[b] << 16));
-      }
-      hw[j2] = hb[0] | (hb[1] << 16);
-      lw[j2] = lb[0] | (lb[1] << 16);
+      const float p0 = __builtin_amdgcn_exp2f(x[8 * h + 2 * j2] - mu);
+      const float p1 = __builtin_amdgcn_exp2f(x[8 * h + 2 * j2 + 1] - mu);
+      st.l_part += p0;
+      st.l_part += p1;
+      const bf2 hi = {(__bf16)p0, (__bf16)p1};
+      hw[j2] = __builtin_bit_cast(uint32_t, hi);
+      const bf2 lo = {(__bf16)(p0 - __uint_as_float(hw[j2] << 16)),
+                      (__bf16)(p1 - __uint_as_float(hw[j2] & 0xffff0000u))};
+      lw[j2] = __builtin_bit_cast(uint32_t, lo);
     }
     ph[h] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     pl[h] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
-  // out^T(dt) += V^T(dt) . P^T: lane (nn, gq) reads dim 16dt + nn, keys 32h + 4gq..+3 and
-  // 32h + 16 + 4gq..+3 (tiles 2h and 2h + 1).
+  // out^T(dt) += V^T(dt) . P^T: lane (nn, gq) needs dim 16dt + nn of keys 32h + 4gq..+3
+  // and 32h + 16 + 4gq..+3 (tiles 2h and 2h + 1). Two transposed 8-byte reads give them:
+  // within each 16-lane group, lane s addresses 4 dims (16dt + 4(s & 3)..) of key row
+  // 32h (+16) + 4gq + s/4, and lane nn receives element nn & 3 of lanes nn/4 + 4k.
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) {
-    const int8_t* vrow = cur.vt + (16 * dt + nn) * kVtStride + 8 * gq;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint2 a0 = *reinterpret_cast<const uint2*>(vrow + 64 * h);
-      const uint2 a1 = *reinterpret_cast<const uint2*>(vrow + 64 * h + 32);
-      const v8bf a = __builtin_bit_cast(v8bf, make_uint4(a0.x, a0.y, a1.x, a1.y));
+      const int8_t* p0 = cur.v + vaddr[dt & 7] + (dt >> 3) * 256 + 32 * h * 512;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(p0));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(p0 + 16 * 512));
+      const v8bf a = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, ph[h]),
                                                            st.acc[dt], 0, 0, 0);
       st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, pl[h]),
                                                            st.acc[dt], 0, 0, 0);
     }
   }
-  if (more) {
-    ld.store_vt(vr, nxt.vt);
-    __builtin_amdgcn_s_waitcnt(0);  // the next K block has landed in LDS
-  }
+  if (more) __builtin_amdgcn_s_waitcnt(0);  // the next K/V block has landed in LDS
   lds_barrier();
 }
 
@@ -218,16 +216,26 @@ __global__ __launch_bounds__(kCbThreads, 1) void chunk_bf16_kernel(
 
   const Loader ld{k, v, n, n_kv_heads, g, w, lane};
   {
-    uint4 vr[3];
     ld.issue_k(0, s_k0);
-    ld.load_v(0, vr);
+    ld.issue_v(0, s_v0);
     // Query operands: lane (nn, gq) holds dims 32u + 8gq..+7 of its row (rows past the
     // chunk re-read the last one; their outputs are not stored).
     v8bf qop[8];
     const size_t qrow = ((size_t)min(my_tok, n - 1) * n_q_heads + h) * kHeadDim;
 #pragma unroll
     for (int u = 0; u < 8; ++u) qop[u] = *reinterpret_cast<const v8bf*>(q + qrow + 32 * u + 8 * gq);
-    ld.store_vt(vr, s_v0);
+    // Byte offsets of this lane's transposed V reads for dim tiles dt = 0..7 (tiles 8..15
+    // add 256): key row 4gq + nn/4 (+32h, +16 as immediates), dims 16dt + 4(nn & 3), with
+    // the row's chunk swizzle (row & 7 = (4gq + nn/4) & 7 for every h and half).
+    int vaddr[8];
+    {
+      const int r = 4 * gq + (nn >> 2), swz = (r & 7) << 1;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const int c = 2 * d + ((nn & 3) >> 1);
+        vaddr[d] = r * 512 + (c ^ swz) * 16 + (nn & 1) * 8;
+      }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
 
@@ -238,9 +246,11 @@ __global__ __launch_bounds__(kCbThreads, 1) void chunk_bf16_kernel(
     for (int dt = 0; dt < 16; ++dt) st.acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
     const Block b0{s_k0, s_v0}, b1{s_k1, s_v1};
     for (int kb = 0; kb < nkb; kb += 2) {
-      block_step(kb, nkb, ld, qop, my_tok, causal != 0, n, qk_scale_log2, gq, nn, st, b0, b1);
+      block_step(kb, nkb, ld, qop, my_tok, t0, causal != 0, n, qk_scale_log2, gq, nn, vaddr, st,
+                 b0, b1);
       if (kb + 1 < nkb)
-        block_step(kb + 1, nkb, ld, qop, my_tok, causal != 0, n, qk_scale_log2, gq, nn, st, b1, b0);
+        block_step(kb + 1, nkb, ld, qop, my_tok, t0, causal != 0, n, qk_scale_log2, gq, nn, vaddr,
+                   st, b1, b0);
     }
     const float l = col_sum(st.l_part);
     if (my_tok < n) {
