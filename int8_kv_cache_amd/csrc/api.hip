@@ -32,7 +32,8 @@ int check_launch(const char* what) {
 
 static int check_heads(int n_q_heads, int n_kv_heads, int head_dim) {
   if (n_q_heads <= 0 || n_kv_heads <= 0) return set_error(I8A_EINVAL, "head counts must be > 0");
-  if (n_kv_heads > 65535) return set_error(I8A_EINVAL, "n_kv_heads > 65535");
+  // The merge kernels put the query heads on grid.y (at most 65535).
+  if (n_q_heads > 65535) return set_error(I8A_EINVAL, "n_q_heads %d > 65535", n_q_heads);
   if (head_dim != 256) return set_error(I8A_EUNSUPPORTED, "head_dim %d unsupported (v1: 256)", head_dim);
   if (n_q_heads != 6 * n_kv_heads)
     return set_error(I8A_EUNSUPPORTED, "n_q_heads %d / n_kv_heads %d: v1 supports GQA groups of 6",

@@ -101,6 +101,9 @@ def test_attn_decode_validation():
 
     assert call(12, 8) == C["I8A_EUNSUPPORTED"]        # 24 q heads over 8 kv heads
     assert call(13, 128) == C["I8A_EUNSUPPORTED"]      # head_dim
+    a = list(base)
+    a[11], a[12] = 6 * 11000, 11000                    # query heads beyond the merge grid
+    assert L.attn_decode(*a) == C["I8A_EINVAL"]
     assert call(9, 0) == C["I8A_EINVAL"]               # max_context_len
     assert call(10, 0) == C["I8A_EINVAL"]              # num_pages
     assert call(14, float("nan")) == C["I8A_EINVAL"]   # sm_scale
