@@ -37,8 +37,6 @@ namespace i8a {
 constexpr int kPfTok = 32;                 // query tokens per workgroup
 constexpr int kPfWaves = 2 * kGroup;       // (head, 16-token half) per wave
 constexpr int kPfThreads = kPfWaves * 64;  // 768
-constexpr int kPfChunks = 2048;            // 16-byte chunks of one 64-key K+V block
-constexpr int kPfPerThread = (kPfChunks + kPfThreads - 1) / kPfThreads;  // 3
 constexpr float kLazyRescale = 8.0f;       // log2 units
 constexpr float kMagicF = 12582912.0f;   // 1.5 * 2^23
 constexpr v4i kMagic4 = {0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};  // its bits
