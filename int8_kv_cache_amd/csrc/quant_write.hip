@@ -55,15 +55,17 @@ __device__ __forceinline__ void rope4(float* x, const float* __restrict__ cs, in
   }
 }
 
-// Workgroup = (16 consecutive tokens, KV head): wave w quantizes the K and V rows of
-// tokens 4w..4w+3 of the group (row loads issued before anything waits). When the 16
+// Workgroup = (16 consecutive tokens, KV head) of 16 / TPW waves: wave w quantizes the K
+// and V rows of tokens TPW w .. TPW w + TPW - 1 of the group (row loads issued before
+// anything waits). kv_quant_write runs 2 tokens per wave, kv_produce (with 6 query rows per
+// token) 1, so that more waves hide the load and reduction latencies. When the 16
 // tokens fill one whole page in order (slots s0..s0+15, s0 % 16 == 0, the common case of
 // prefill chunks and bulk fills) the workgroup assembles the page's dim-major V block
 // in LDS and writes K, V and the scales as whole 16-byte runs; otherwise every token is
 // scattered to its own slot.
 // With PRODUCE (kv_produce) the K rows are rotated by their token's position first, and
 // the workgroup also rotates and quantizes the query rows of the KV head's group for its
-// 16 tokens (wave w: tokens 4w..4w+3, all 6 heads), codes row-major into q_codes.
+// 16 tokens (each wave: its tokens, all 6 heads), codes row-major into q_codes.
 struct Produce {
   const void* q;
   const int32_t* positions;
@@ -84,8 +86,11 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, const float* x) {
                                               bf16_bits(x[2]) | (bf16_bits(x[3]) << 16));
 }
 
-template <int IN_BF16, int PRODUCE>
-__global__ __launch_bounds__(256) void kv_quant_write_kernel(
+constexpr int kWriteTpw = 2;    // tokens per wave of kv_quant_write
+constexpr int kProduceTpw = 1;  // tokens per wave of kv_produce
+
+template <int IN_BF16, int PRODUCE, int TPW>
+__global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
     const void* __restrict__ k, const void* __restrict__ v, int n_tokens, int n_kv_heads,
     const int32_t* __restrict__ slots, int8_t* __restrict__ k_cache,
     int8_t* __restrict__ v_cache, float* __restrict__ k_scale, float* __restrict__ v_scale,
@@ -106,35 +111,35 @@ __global__ __launch_bounds__(256) void kv_quant_write_kernel(
     const bool all = __all(ok);
     if (lane == 0) s_run = all ? 1 : 0;
   }
-  float kx[4][4], vx[4][4];
-  int myslot[4];
+  float kx[TPW][4], vx[TPW][4];
+  int myslot[TPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = min(tok0 + 4 * w + i, n_tokens - 1);
+  for (int i = 0; i < TPW; ++i) {
+    const int t = min(tok0 + TPW * w + i, n_tokens - 1);
     const size_t row = (size_t)t * n_kv_heads + head;
     load_row4<IN_BF16>(k, row, lane, kx[i]);
     load_row4<IN_BF16>(v, row, lane, vx[i]);
-    myslot[i] = tok0 + 4 * w + i < n_tokens ? slots[tok0 + 4 * w + i] : -1;
+    myslot[i] = tok0 + TPW * w + i < n_tokens ? slots[tok0 + TPW * w + i] : -1;
   }
   // Query rows of the group for this wave's tokens, loaded with the K/V rows (one round
   // trip); tokens past the batch re-read the last one and are not stored.
-  float qx[PRODUCE ? 4 : 1][kGroup][4];
+  float qx[PRODUCE ? TPW : 1][kGroup][4];
   const bool want_q = PRODUCE && (pr.q_codes != nullptr || pr.q_rot != nullptr);
   if (want_q) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = min(tok0 + 4 * w + i, n_tokens - 1);
+    for (int i = 0; i < TPW; ++i) {
+      const int t = min(tok0 + TPW * w + i, n_tokens - 1);
 #pragma unroll
       for (int hh = 0; hh < kGroup; ++hh)
         load_row4<IN_BF16>(pr.q, (size_t)t * pr.n_q_heads + head * kGroup + hh, lane,
                            qx[PRODUCE ? i : 0][hh]);
     }
   }
-  const float* cs_row[4] = {nullptr, nullptr, nullptr, nullptr};  // RoPE rows of the tokens
+  const float* cs_row[TPW] = {};  // RoPE rows of the tokens
   if (PRODUCE && pr.rotary_dim > 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = min(tok0 + 4 * w + i, n_tokens - 1);
+    for (int i = 0; i < TPW; ++i) {
+      const int t = min(tok0 + TPW * w + i, n_tokens - 1);
       const int pos = min(max(pr.positions[t], 0), pr.max_pos - 1);  // clamped: memory-safe
       cs_row[i] = pr.cos_sin + (size_t)pos * pr.rotary_dim;
       rope4(kx[i], cs_row[i], pr.rotary_dim, lane);
@@ -142,23 +147,23 @@ __global__ __launch_bounds__(256) void kv_quant_write_kernel(
   }
   if (PRODUCE && pr.k_rot != nullptr) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = tok0 + 4 * w + i;
+    for (int i = 0; i < TPW; ++i) {
+      const int t = tok0 + TPW * w + i;
       if (t < n_tokens) store_bf16x4(pr.k_rot + ((size_t)t * n_kv_heads + head) * kHeadDim + lane * 4, kx[i]);
     }
   }
-  uint32_t kq[4], vq[4];
-  float ks[4], vs[4];
+  uint32_t kq[TPW], vq[TPW];
+  float ks[TPW], vs[TPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TPW; ++i) {
     kq[i] = quantize4(kx[i][0], kx[i][1], kx[i][2], kx[i][3], &ks[i]);
     vq[i] = quantize4(vx[i][0], vx[i][1], vx[i][2], vx[i][3], &vs[i]);
   }
   if (want_q) {
     // The group's query rows of this wave's tokens: rotate, quantize, store.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = tok0 + 4 * w + i;
+    for (int i = 0; i < TPW; ++i) {
+      const int t = tok0 + TPW * w + i;
       if (t >= n_tokens) break;  // whole wave
 #pragma unroll
       for (int hh = 0; hh < kGroup; ++hh) {
@@ -177,36 +182,44 @@ __global__ __launch_bounds__(256) void kv_quant_write_kernel(
   }
   __syncthreads();
   if (s_run) {
-    const int page = __shfl(myslot[0], 0) >> 4;  // slot s0 + 4w, same page for every wave
+    const int page = __shfl(myslot[0], 0) >> 4;  // slot s0 + TPW w, same page for every wave
     const size_t blk = ((size_t)page * n_kv_heads + head) * kBlockBytes;
-    // K: token 4w + i, dims 4l..4l+3 -> chunk l/4, byte (l%4)*4 of the token's 16-byte run.
+    // K: token TPW w + i, dims 4l..4l+3 -> chunk l/4, byte (l%4)*4 of the token's 16-byte run.
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint32_t*>(k_cache + blk + (lane >> 2) * 256 + (4 * w + i) * 16 +
+    for (int i = 0; i < TPW; ++i)
+      *reinterpret_cast<uint32_t*>(k_cache + blk + (lane >> 2) * 256 + (TPW * w + i) * 16 +
                                    (lane & 3) * 4) = kq[i];
-    // V: dim 4l + j gets the 4 bytes of tokens 4w..4w+3 in one LDS dword.
+    // V: dim 4l + j gets the TPW bytes of tokens TPW w .. TPW w + TPW - 1.
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = __builtin_amdgcn_perm(vq[1], vq[0], 0x0c0c0400u + j * 0x00000101u);
-      const uint32_t hi = __builtin_amdgcn_perm(vq[3], vq[2], 0x0c0c0400u + j * 0x00000101u);
-      s_v[(4 * lane + j) * 4 + w] = (lo & 0xffffu) | (hi << 16);
+      if (TPW == 4) {
+        const uint32_t lo = __builtin_amdgcn_perm(vq[1], vq[0], 0x0c0c0400u + j * 0x00000101u);
+        const uint32_t hi = __builtin_amdgcn_perm(vq[3 % TPW], vq[2 % TPW], 0x0c0c0400u + j * 0x00000101u);
+        s_v[(4 * lane + j) * 4 + w] = (lo & 0xffffu) | (hi << 16);
+      } else if (TPW == 2) {
+        const uint32_t lo = __builtin_amdgcn_perm(vq[1 % TPW], vq[0], 0x0c0c0400u + j * 0x00000101u);
+        reinterpret_cast<uint16_t*>(s_v)[(4 * lane + j) * 8 + w] = (uint16_t)lo;
+      } else {
+        reinterpret_cast<uint8_t*>(s_v)[(4 * lane + j) * 16 + w] = (uint8_t)(vq[0] >> (8 * j));
+      }
     }
     if (lane == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s_sc[0][4 * w + i] = ks[i];
-        s_sc[1][4 * w + i] = vs[i];
+      for (int i = 0; i < TPW; ++i) {
+        s_sc[0][TPW * w + i] = ks[i];
+        s_sc[1][TPW * w + i] = vs[i];
       }
     }
     __syncthreads();
-    *reinterpret_cast<uint4*>(v_cache + blk + tid * 16) = reinterpret_cast<const uint4*>(s_v)[tid];
+    if (tid < kBlockBytes / 16)
+      *reinterpret_cast<uint4*>(v_cache + blk + tid * 16) = reinterpret_cast<const uint4*>(s_v)[tid];
     if (tid < 32) {
       const size_t si = ((size_t)page * n_kv_heads + head) * kPage + (tid & 15);
       (tid < 16 ? k_scale : v_scale)[si] = s_sc[tid >> 4][tid & 15];
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TPW; ++i) {
       const int slot = myslot[i];
       if (slot < 0 || (long long)slot >= n_slots) continue;  // skipped token (whole wave)
       const int page = slot >> 4, o = slot & 15;
@@ -243,14 +256,14 @@ __global__ __launch_bounds__(256) void q_quant_kernel(const uint16_t* __restrict
 int launch_kv_quant_write(const void* k, const void* v, int in_bf16, int n_tokens, int n_kv_heads,
                           const int32_t* slots, int8_t* k_cache, int8_t* v_cache, float* k_scale,
                           float* v_scale, int num_pages, hipStream_t stream) {
-  const dim3 grid((n_tokens + 15) / 16, n_kv_heads), block(256);
+  const dim3 grid((n_tokens + 15) / 16, n_kv_heads), block(64 * 16 / kWriteTpw);
   const long long n_slots = (long long)num_pages * kPage;
   const Produce none{nullptr, nullptr, nullptr, 0, 1, 0, nullptr, nullptr, nullptr, nullptr};
   if (in_bf16)
-    hipLaunchKernelGGL((kv_quant_write_kernel<1, 0>), grid, block, 0, stream, k, v, n_tokens,
+    hipLaunchKernelGGL((kv_quant_write_kernel<1, 0, kWriteTpw>), grid, block, 0, stream, k, v, n_tokens,
                        n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots, none);
   else
-    hipLaunchKernelGGL((kv_quant_write_kernel<0, 0>), grid, block, 0, stream, k, v, n_tokens,
+    hipLaunchKernelGGL((kv_quant_write_kernel<0, 0, kWriteTpw>), grid, block, 0, stream, k, v, n_tokens,
                        n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots, none);
   return check_launch("kv_quant_write");
 }
@@ -261,15 +274,15 @@ int launch_kv_produce(const void* q, const void* k, const void* v, int in_bf16, 
                       int8_t* v_cache, float* k_scale, float* v_scale, int num_pages,
                       int8_t* q_codes, float* q_scales, uint16_t* q_rot, uint16_t* k_rot,
                       hipStream_t stream) {
-  const dim3 grid((n_tokens + 15) / 16, n_kv_heads), block(256);
+  const dim3 grid((n_tokens + 15) / 16, n_kv_heads), block(64 * 16 / kProduceTpw);
   const long long n_slots = (long long)num_pages * kPage;
   const Produce pr{q, positions, cos_sin, rotary_dim, max_pos, n_q_heads, q_codes, q_scales,
                    q_rot, k_rot};
   if (in_bf16)
-    hipLaunchKernelGGL((kv_quant_write_kernel<1, 1>), grid, block, 0, stream, k, v, n_tokens,
+    hipLaunchKernelGGL((kv_quant_write_kernel<1, 1, kProduceTpw>), grid, block, 0, stream, k, v, n_tokens,
                        n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots, pr);
   else
-    hipLaunchKernelGGL((kv_quant_write_kernel<0, 1>), grid, block, 0, stream, k, v, n_tokens,
+    hipLaunchKernelGGL((kv_quant_write_kernel<0, 1, kProduceTpw>), grid, block, 0, stream, k, v, n_tokens,
                        n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots, pr);
   return check_launch("kv_produce");
 }
