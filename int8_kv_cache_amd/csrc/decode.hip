@@ -77,7 +77,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
   __shared__ __align__(16) float s_ks[kPart];
   __shared__ __align__(16) float s_vs[kPart];
   __shared__ float s_m[kDecWaves][kGroup], s_l[kDecWaves][kGroup], s_f[kDecWaves];
-  __shared__ __align__(16) float s_o[kDecWaves][kGroup][kHeadDim];
+  __shared__ __align__(16) float s_o[kDecWaves][kGroup][kHeadDim + 4];  // rows padded by 16 B
   __shared__ __align__(16) float4 s_junk[64];  // sink for the stores of unused columns
   __shared__ uint32_t s_bias;  // 0x80808080, read back after the barrier (see i8x4_to_f16)
 
@@ -257,9 +257,9 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(
     if (lane == 0) s_f[w] = svm;
   } else {
     // No tokens: an empty state (its weight in the merge below is exp2(-inf) = 0).
-    float4* o = reinterpret_cast<float4*>(&s_o[w][0][0]);
 #pragma unroll
-    for (int i = 0; i < kGroup * kHeadDim / 4 / 64; ++i) o[i * 64 + lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = 0; r < kGroup; ++r)
+      reinterpret_cast<float4*>(&s_o[w][r][0])[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (lane < kGroup) {
       s_m[w][lane] = -INFINITY;
       s_l[w][lane] = 0.f;

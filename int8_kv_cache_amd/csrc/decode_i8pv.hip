@@ -100,7 +100,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void split_i8pv_kernel(
   __shared__ __align__(16) float s_vs[kKeys];
   __shared__ float s_f[WAVES];                               // the wave's max V scale
   __shared__ float s_m[WAVES][kRowTile], s_l[WAVES][kRowTile], s_c[WAVES][kRowTile];
-  __shared__ __align__(16) float s_o[WAVES][kRowTile][kHeadDim];
+  // Rows padded by 16 bytes: the 16 rows a wave writes at one dim range fall on
+  // different banks.
+  __shared__ __align__(16) float s_o[WAVES][kRowTile][kHeadDim + 4];
 
   const int wtok0 = w * 64;
   const int nvalid = min(64, n_tok - wtok0);  // tokens of the block inside the context
@@ -301,9 +303,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void split_i8pv_kernel(
         s_c[w][n] = DIG == 1 ? sb : sb * (1.0f / 128.0f);
       }
     } else {
-      float4* o = reinterpret_cast<float4*>(&s_o[w][0][0]);
 #pragma unroll
-      for (int i = 0; i < kRowTile * kHeadDim / 4 / 64; ++i) o[i * 64 + lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int r = 0; r < kRowTile; ++r)
+        reinterpret_cast<float4*>(&s_o[w][r][0])[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (lane < kRowTile) {
         s_m[w][lane] = -INFINITY;
         s_l[w][lane] = 0.f;
