@@ -45,6 +45,26 @@ def test_chunk_bf16_matches_exact(n, causal):
     assert err <= TOL * vmax
 
 
+@pytest.mark.parametrize("n_kv", [1, 3])
+def test_chunk_bf16_other_kv_head_counts(n_kv):
+    need_gpu()
+    n = 77
+    say(f"attn_chunk_bf16 n={n} causal with {n_kv} KV heads x 6 query heads")
+    rng = np.random.default_rng(230 + n_kv)
+    q = rng.standard_normal((n, 6 * n_kv, 256), dtype=np.float32)
+    k = rng.standard_normal((n, n_kv, 256), dtype=np.float32)
+    v = rng.standard_normal((n, n_kv, 256), dtype=np.float32)
+    qb, kb, vb = (workloads.f32_to_bf16_bits(a) for a in (q, k, v))
+    out = lib.attn_chunk_bf16(_bf16(qb), _bf16(kb), _bf16(vb), causal=True)
+    torch.cuda.synchronize()
+    qd, kd, vd = (quant.bf16_bits_to_f32(a).astype(np.float64) for a in (qb, kb, vb))
+    ref = attention.attention_exact(qd, kd, vd, 1 / 16, np.arange(n))
+    err = float(np.max(np.abs(out.cpu().numpy() - ref)))
+    vmax = float(np.max(np.abs(vd)))
+    say(f"  err {err:.3e} (bound {TOL * vmax:.3e})")
+    assert err <= TOL * vmax
+
+
 def test_producer_rotated_rows_bit_exact():
     need_gpu()
     case = workloads.make_producer_case(210, 300, start=0, rotary_dim=128)

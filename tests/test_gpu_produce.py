@@ -3,6 +3,8 @@ the oracle bit for bit, and the int8-query (*_q8) attention forms: given q_quant
 they equal the bf16 forms bit for bit, and after the producer they match the oracle on
 the rotated rows. ("INT8 KV and INT8 MMAC attention on a gfx936 DCU" §2.2 fused producer;
 §3.3: the decode consumes INT8 Q and its scale.)"""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -28,11 +30,11 @@ def _run(case, in_bf16):
         tq, tk, tv = (_bits_tensor(a) for a in (qb, kb, vb))
     else:
         tq, tk, tv = up(q), up(k), up(v)
-    cache = gpu_cache(case.num_pages, 4)
+    cache = gpu_cache(case.num_pages, case.n_kv_heads)
     qc, qs = lib.kv_produce(tq, tk, tv, up(case.positions), up(table), up(case.slots), cache,
                             rotary_dim=case.rotary_dim)
     torch.cuda.synchronize()
-    ref_cache = oracle_cache(case.num_pages, 4)
+    ref_cache = oracle_cache(case.num_pages, case.n_kv_heads)
     rqc, rqs = rope.produce(q, k, v, case.positions, table, case.rotary_dim, case.slots, ref_cache)
     return cache, (qc, qs), ref_cache, (rqc, rqs), table
 
@@ -50,6 +52,19 @@ def test_produce_bit_exact(T, start, layout, rd, in_bf16):
     cache, (qc, qs), ref_cache, (rqc, rqs), _ = _run(case, in_bf16)
     got = cache_to_host(cache)
     for name, a, b in zip(("k codes", "v codes", "k scales", "v scales"), got, ref_cache):
+        assert np.array_equal(a, b), name
+    assert np.array_equal(qc.cpu().numpy(), rqc)
+    assert np.array_equal(qs.cpu().numpy().view(np.uint32), rqs.view(np.uint32))
+
+
+@pytest.mark.parametrize("n_kv", [1, 2, 3])
+def test_produce_other_kv_head_counts(n_kv):
+    need_gpu()
+    say(f"kv_produce with {n_kv} KV heads x 6 query heads, 45 tokens from position 5")
+    case = dataclasses.replace(workloads.make_producer_case(130 + n_kv, 45, start=5, rotary_dim=128),
+                               n_q_heads=6 * n_kv, n_kv_heads=n_kv)
+    cache, (qc, qs), ref_cache, (rqc, rqs), _ = _run(case, True)
+    for name, a, b in zip(("k codes", "v codes", "k scales", "v scales"), cache_to_host(cache), ref_cache):
         assert np.array_equal(a, b), name
     assert np.array_equal(qc.cpu().numpy(), rqc)
     assert np.array_equal(qs.cpu().numpy().view(np.uint32), rqs.view(np.uint32))
