@@ -197,6 +197,24 @@ def test_int8p_matches_brute_force():
     assert np.max(np.abs(out - ref)) <= 1e-12
 
 
+def test_int8p_hand_worked_two_blocks():
+    """A case worked by hand. One query, 4 keys, blocks of 2, scores 0, -ln 4, -ln 2,
+    -ln 8 (sm_scale 1), so p = 1, 1/4, 1/2, 1/8 and l = 15/8; V scales 1, 1, 2, 5 and V
+    codes 2, -3, 5, 7. Weights w = p * sV: block 0 (1, 1/4), s_b = 1/127, codes 127 and
+    rint(31.75) = 32; block 1 (1, 5/8), s_b = 1/127, codes 127 and rint(79.375) = 79.
+    Output = ((127*2 - 32*3) + (127*5 + 79*7)) / 127 / (15/8) = 1346 / 238.125.
+    (Quantizing p before the V scale is folded in would give 1353 / 238.125; exact
+    attention gives 10.625 / 1.875.)"""
+    q = np.array([[[1.0]]])
+    k = np.array([[[0.0]], [[-np.log(4.0)]], [[-np.log(2.0)]], [[-np.log(8.0)]]])
+    vc = np.array([[[2]], [[-3]], [[5]], [[7]]], dtype=np.int8)
+    vs = np.array([[1.0], [1.0], [2.0], [5.0]], np.float32)
+    out = A.attention_int8p(q, k, vc, vs, 1.0, [3], block=2)
+    assert abs(out[0, 0, 0] - 1346 / 238.125) <= 1e-12
+    exact = A.attention_exact(q, k, quant.dequantize(vc, vs), 1.0, [3])
+    assert abs(exact[0, 0, 0] - 10.625 / 1.875) <= 1e-12
+
+
 def test_int8p_exact_when_block_weights_equal():
     rng = np.random.default_rng(13)
     N = 130
