@@ -33,7 +33,8 @@ Q=0, equal keys, dominant key), softmax normalisation, merge = unsplit, page
 permutation invariance, chunk row = decode at the matching context, verify rows =
 decode at each row's context; RoPE against complex multiplication, exact quarter
 turns, relative-position invariance of scores.
-The int8-P emulation is pinned by brute force, an exact special case and its
-error bound; beyond that its agreement with the pages is "parity unpinned".
+The int8-P emulation is pinned by brute force, an exact special case, its error
+bound and a two-block case worked by hand from the rule; the pages print no worked
+example of it.
 """
 from . import quant, paged, attention, rope  # noqa: F401
