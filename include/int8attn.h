@@ -335,6 +335,35 @@ int attn_prefill_chunk(const uint16_t* q, int n_new,
                        int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
                        float sm_scale, float* out, void* stream);
 
+/* attn_prefill_chunk_split -- attn_prefill_chunk with the keys cut into partitions for
+ * short causal chunks, whose one-pass grid (one workgroup per 32 query tokens and KV
+ * head) would leave most of the GPU idle.
+ * [DCU §3.3: key partitions processed by separate workgroups, each keeping its own
+ *  running max, sum and output, combined by a log-sum-exp merge as in the decode; DCU
+ *  §3.2 and §1.3 for everything inside a partition.]
+ *
+ *  Arguments as for attn_prefill_chunk, plus:
+ *  workspace     device scratch, 16-byte aligned, of at least
+ *                attn_prefill_chunk_split_workspace_bytes(...) bytes; its contents on
+ *                entry do not matter and are overwritten. Calls that share a workspace
+ *                must be ordered (same stream).
+ *  The route: a causal chunk with fewer than 128 (32-token query block, KV head) pairs
+ *  is cut into partitions of whole 64-key blocks so that about 256 workgroups run, and
+ *  a second kernel merges the partitions; any other chunk (and every non-causal one)
+ *  takes the one pass of attn_prefill_chunk, bit for bit, and needs no workspace. The
+ *  int8 weight codes are per aligned 64-key block in both routes, so the split result
+ *  differs from the one pass only by rounding in the merge.
+ *  workspace_bytes below the required size returns I8A_EWORKSPACE. */
+size_t attn_prefill_chunk_split_workspace_bytes(int n_new, int context_len, int causal,
+                                                int n_q_heads, int n_kv_heads, int head_dim);
+int attn_prefill_chunk_split(const uint16_t* q, int n_new,
+                             const int8_t* k_cache, const int8_t* v_cache,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_table, int context_len, int causal,
+                             int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                             float sm_scale, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* *_q8 forms: the same computations with the query given as int8 codes and fp32 scales
  * (the format kv_produce writes: q_codes [rows][head_dim], q_scales [rows], rows laid
  * out as the bf16 q of the plain form) instead of bf16 rows that the call quantizes.
@@ -371,6 +400,13 @@ int attn_prefill_chunk_q8(const int8_t* q_codes, const float* q_scales, int n_ne
                           const int32_t* block_table, int context_len, int causal,
                           int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
                           float sm_scale, float* out, void* stream);
+int attn_prefill_chunk_split_q8(const int8_t* q_codes, const float* q_scales, int n_new,
+                                const int8_t* k_cache, const int8_t* v_cache,
+                                const float* k_scale, const float* v_scale,
+                                const int32_t* block_table, int context_len, int causal,
+                                int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                                float sm_scale, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

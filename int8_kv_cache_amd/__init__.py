@@ -18,7 +18,8 @@ import torch
 __all__ = ["lib", "PagedCache", "alloc_cache", "kv_quant_write", "q_quant", "attn_decode",
            "attn_decode_workspace_bytes", "attn_verify", "attn_verify_workspace_bytes",
            "attn_decode_int8p", "attn_decode_int8p_workspace_bytes", "attn_decode_partition_rows",
-           "attn_prefill_chunk", "kv_produce", "attn_chunk_bf16", "prefill_step",
+           "attn_prefill_chunk", "attn_prefill_chunk_split",
+           "attn_prefill_chunk_split_workspace_bytes", "kv_produce", "attn_chunk_bf16", "prefill_step",
            "prefill_step_workspace_bytes", "Int8AttnError",
            "HEAD_DIM", "PAGE", "PARTITION", "EXPORTED_SYMBOLS"]
 
@@ -33,7 +34,8 @@ EXPORTED_SYMBOLS = ("int8attn_last_error", "int8attn_version", "kv_quant_write",
                     "attn_decode_workspace_bytes", "attn_decode", "attn_verify_workspace_bytes",
                     "attn_verify", "attn_decode_partition_rows",
                     "attn_decode_int8p_workspace_bytes", "attn_decode_int8p",
-                    "attn_prefill_chunk")
+                    "attn_prefill_chunk", "attn_prefill_chunk_split_workspace_bytes",
+                    "attn_prefill_chunk_split", "attn_prefill_chunk_split_q8")
 
 _c_void = ctypes.c_void_p
 _c_int = ctypes.c_int
@@ -86,6 +88,15 @@ _SIGNATURES = {
     "attn_prefill_chunk": (_c_int, [_c_void, _c_int, _c_void, _c_void, _c_void, _c_void,
                                     _c_void, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     _c_float, _c_void, _c_void]),
+    "attn_prefill_chunk_split_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int,
+                                                           _c_int, _c_int]),
+    "attn_prefill_chunk_split": (_c_int, [_c_void, _c_int, _c_void, _c_void, _c_void, _c_void,
+                                          _c_void, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                          _c_int, _c_float, _c_void, _c_void, _c_size, _c_void]),
+    "attn_prefill_chunk_split_q8": (_c_int, [_c_void, _c_void, _c_int, _c_void, _c_void,
+                                             _c_void, _c_void, _c_void, _c_int, _c_int, _c_int,
+                                             _c_int, _c_int, _c_int, _c_float, _c_void, _c_void,
+                                             _c_size, _c_void]),
 }
 
 
@@ -447,4 +458,37 @@ def attn_prefill_chunk(q: torch.Tensor, cache, block_table: torch.Tensor, contex
                                     int(context_len), int(bool(causal)), cache.num_pages, Hq,
                                     cache.n_kv_heads, D, sm,
                                     _dev(out, "out", torch.float32), _stream(stream)))
+    return out
+
+
+def attn_prefill_chunk_split_workspace_bytes(n_new: int, context_len: int, causal: bool,
+                                             n_q_heads: int, n_kv_heads: int,
+                                             head_dim: int = HEAD_DIM) -> int:
+    return int(lib().attn_prefill_chunk_split_workspace_bytes(n_new, context_len, int(bool(causal)),
+                                                              n_q_heads, n_kv_heads, head_dim))
+
+
+def attn_prefill_chunk_split(q: torch.Tensor, cache, block_table: torch.Tensor, context_len: int,
+                             causal: bool = True, sm_scale: float | None = None,
+                             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                             stream=None, q_scales: torch.Tensor | None = None) -> torch.Tensor:
+    """attn_prefill_chunk with the keys split over workgroups for short causal chunks
+    (a merge kernel combines the partitions); other chunks take the one pass."""
+    qs = _query(q, q_scales, 3, "[n_new, Hq, head_dim]")
+    n_new, Hq, D = q.shape
+    if block_table.dim() != 1 or block_table.numel() < (context_len + PAGE - 1) // PAGE:
+        raise ValueError("block_table must be [ceil(context_len/16)]")
+    if out is None:
+        out = torch.empty((n_new, Hq, D), dtype=torch.float32, device=q.device)
+    need = attn_prefill_chunk_split_workspace_bytes(n_new, context_len, causal, Hq,
+                                                    cache.n_kv_heads, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    sm = float(sm_scale if sm_scale is not None else D ** -0.5)
+    fn, head = ((lib().attn_prefill_chunk_split, (_dev(q, "q"),)) if qs is None
+                else (lib().attn_prefill_chunk_split_q8, (_dev(q, "q"), qs)))
+    _check(fn(*head, n_new, *cache.ptrs(), _dev(block_table, "block_table", torch.int32),
+              int(context_len), int(bool(causal)), cache.num_pages, Hq, cache.n_kv_heads, D, sm,
+              _dev(out, "out", torch.float32), _dev(workspace, "workspace"),
+              workspace.numel() * workspace.element_size(), _stream(stream)))
     return out

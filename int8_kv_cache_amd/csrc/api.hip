@@ -408,17 +408,44 @@ int attn_decode_int8p_q8(const int8_t* q_codes, const float* q_scales, int nq,
                     workspace_bytes, stream);
 }
 
+// The split route of a chunk: 0 the one pass, 1 key partitions of the chunk kernel, 2 the
+// int8-P decode kernel (chunks of at most 8 rows: the same weight rule, one workgroup per
+// (KV head, key partition) for all the rows). Causal chunks only.
+static int split_route(int n_new, int context_len, int causal, int n_kv_heads) {
+  if (!causal || n_new <= 0) return 0;
+  if (n_new <= 8) return 2;
+  int pb;
+  return prefill_split_parts(n_new, context_len, causal, n_kv_heads, &pb) > 1 ? 1 : 0;
+}
+
+static size_t split_ws_bytes(int n_new, int context_len, int causal, int n_q_heads, int n_kv_heads) {
+  switch (split_route(n_new, context_len, causal, n_kv_heads)) {
+    case 1: return prefill_split_ws_bytes(n_new, context_len, causal, n_q_heads, n_kv_heads);
+    case 2: return partials_bytes(n_new, context_len, n_q_heads, partition_law(1, context_len, n_kv_heads));
+    default: return 0;
+  }
+}
+
 static int prefill_impl(const void* q, const float* q_scales, int n_new, const int8_t* k_cache,
                         const int8_t* v_cache, const float* k_scale, const float* v_scale,
                         const int32_t* block_table, int context_len, int causal, int num_pages,
                         int n_q_heads, int n_kv_heads, int head_dim, float sm_scale, float* out,
-                        void* stream) {
+                        int split, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
   if (rc) return rc;
   if (n_new < 0 || context_len < 1 || n_new > context_len || num_pages <= 0 ||
       (causal != 0 && causal != 1))
     return set_error(I8A_EINVAL, "attn_prefill_chunk: n_new %d, context_len %d, num_pages %d, causal %d",
                      n_new, context_len, num_pages, causal);
+  size_t need = 0;
+  if (split) {
+    need = split_ws_bytes(n_new, context_len, causal, n_q_heads, n_kv_heads);
+    if (need > 0 && (!workspace || ((uintptr_t)workspace & 15u) != 0))
+      return set_error(I8A_EINVAL, "attn_prefill_chunk_split: workspace null or not 16-byte aligned");
+    if (workspace_bytes < need)
+      return set_error(I8A_EWORKSPACE, "attn_prefill_chunk_split: workspace %zu bytes < %zu needed",
+                       workspace_bytes, need);
+  }
   if (context_len > 2147483000 - 64) return set_error(I8A_EINVAL, "attn_prefill_chunk: context too long");
   if ((long long)num_pages * n_kv_heads * 16 >= (1ll << 32))
     return set_error(I8A_EUNSUPPORTED, "attn_prefill_chunk: num_pages %d x %d heads exceeds the scale index range",
@@ -427,8 +454,15 @@ static int prefill_impl(const void* q, const float* q_scales, int n_new, const i
   if (n_new == 0) return I8A_OK;
   if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_table || !out)
     return set_error(I8A_EINVAL, "attn_prefill_chunk: null pointer");
+  if (split && split_route(n_new, context_len, causal, n_kv_heads) == 2)
+    return launch_decode_i8pv(1, partition_law(1, context_len, n_kv_heads), q, q_scales, n_new,
+                              k_cache, v_cache, k_scale, v_scale, block_table,
+                              (context_len + 15) / 16, nullptr, 1, context_len, num_pages,
+                              n_q_heads, n_kv_heads, sm_scale, out, static_cast<float*>(workspace),
+                              (hipStream_t)stream);
   return launch_prefill(q, q_scales, n_new, k_cache, v_cache, k_scale, v_scale, block_table,
                         context_len, causal, num_pages, n_q_heads, n_kv_heads, sm_scale, out,
+                        need > 0 ? static_cast<float*>(workspace) : nullptr, workspace_bytes,
                         (hipStream_t)stream);
 }
 
@@ -438,7 +472,7 @@ int attn_prefill_chunk(const uint16_t* q, int n_new, const int8_t* k_cache, cons
                        int head_dim, float sm_scale, float* out, void* stream) {
   return prefill_impl(q, nullptr, n_new, k_cache, v_cache, k_scale, v_scale, block_table,
                       context_len, causal, num_pages, n_q_heads, n_kv_heads, head_dim, sm_scale,
-                      out, stream);
+                      out, 0, nullptr, 0, stream);
 }
 
 int attn_prefill_chunk_q8(const int8_t* q_codes, const float* q_scales, int n_new,
@@ -449,7 +483,40 @@ int attn_prefill_chunk_q8(const int8_t* q_codes, const float* q_scales, int n_ne
   if (!q_scales && n_new > 0) return set_error(I8A_EINVAL, "attn_prefill_chunk_q8: null q_scales");
   return prefill_impl(q_codes, q_scales, n_new, k_cache, v_cache, k_scale, v_scale, block_table,
                       context_len, causal, num_pages, n_q_heads, n_kv_heads, head_dim, sm_scale,
-                      out, stream);
+                      out, 0, nullptr, 0, stream);
+}
+
+size_t attn_prefill_chunk_split_workspace_bytes(int n_new, int context_len, int causal,
+                                                int n_q_heads, int n_kv_heads, int head_dim) {
+  if (n_new <= 0 || context_len < n_new || (causal != 0 && causal != 1) || head_dim != 256 ||
+      n_kv_heads <= 0 || n_q_heads != n_kv_heads * 6)
+    return 0;
+  return split_ws_bytes(n_new, context_len, causal, n_q_heads, n_kv_heads);
+}
+
+int attn_prefill_chunk_split(const uint16_t* q, int n_new, const int8_t* k_cache,
+                             const int8_t* v_cache, const float* k_scale, const float* v_scale,
+                             const int32_t* block_table, int context_len, int causal,
+                             int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                             float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return prefill_impl(q, nullptr, n_new, k_cache, v_cache, k_scale, v_scale, block_table,
+                      context_len, causal, num_pages, n_q_heads, n_kv_heads, head_dim, sm_scale,
+                      out, 1, workspace, workspace_bytes, stream);
+}
+
+int attn_prefill_chunk_split_q8(const int8_t* q_codes, const float* q_scales, int n_new,
+                                const int8_t* k_cache, const int8_t* v_cache,
+                                const float* k_scale, const float* v_scale,
+                                const int32_t* block_table, int context_len, int causal,
+                                int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                                float sm_scale, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!q_scales && n_new > 0)
+    return set_error(I8A_EINVAL, "attn_prefill_chunk_split_q8: null q_scales");
+  return prefill_impl(q_codes, q_scales, n_new, k_cache, v_cache, k_scale, v_scale, block_table,
+                      context_len, causal, num_pages, n_q_heads, n_kv_heads, head_dim, sm_scale,
+                      out, 1, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

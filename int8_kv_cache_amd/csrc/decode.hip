@@ -333,7 +333,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
 #pragma unroll
     for (int i = 0; i < 64; ++i) oj[i] = po[(size_t)(j0 + min(i, cnt - 1)) * kHeadDim];
   };
-  int ctx = ctx_lens[s];
+  int ctx = ctx_lens != nullptr ? ctx_lens[s] : ctx_cap;  // (null: one sequence of ctx_cap)
   load_chunk(0, min(64, max_parts));
   ctx = ctx < 0 ? 0 : (ctx > ctx_cap ? ctx_cap : ctx);
   const int keys = max(0, ctx - nq + qi + 1);  // keys this query row sees

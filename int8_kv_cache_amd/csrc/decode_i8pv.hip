@@ -77,7 +77,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void split_i8pv_kernel(
   int pr[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) pr[t] = trow[min(blk0 + t, max_blocks - 1)];
-  int ctx = ctx_lens[s];
+  int ctx = ctx_lens != nullptr ? ctx_lens[s] : ctx_cap;  // (null: one sequence of ctx_cap)
   asm volatile("" ::"s"(ctx), "s"(pr[0]), "s"(pr[1]), "s"(pr[2]), "s"(pr[3]));
   ctx = ctx < 0 ? 0 : (ctx > ctx_cap ? ctx_cap : ctx);
   const int tok0 = j * kKeys;

@@ -50,6 +50,11 @@ int launch_prefill(const void* q, const float* q_scales, int n_new, const int8_t
                    const int8_t* v_cache,
                    const float* k_scale, const float* v_scale, const int32_t* block_table,
                    int ctx, int causal, int num_pages, int n_q_heads, int n_kv_heads,
-                   float sm_scale, float* out, hipStream_t stream);
+                   float sm_scale, float* out, float* ws, size_t ws_bytes, hipStream_t stream);
+// Key partitions of the split route for a chunk (1: the single pass); *part_blocks gets
+// the 64-key blocks per partition.
+int prefill_split_parts(int n_new, int ctx, int causal, int n_kv_heads, int* part_blocks);
+// Workspace bytes of the split route (0 when the chunk takes the single pass).
+size_t prefill_split_ws_bytes(int n_new, int ctx, int causal, int n_q_heads, int n_kv_heads);
 
 }  // namespace i8a

@@ -30,6 +30,7 @@
 //    one fma folds it in; the offsets s_b * 1.5 * 2^23 are summed per row and taken
 //    out every 8 blocks and at the end.
 #include "common.hpp"
+#include "int8attn.h"
 #include "launch.hpp"
 
 namespace i8a {
@@ -128,6 +129,10 @@ struct RowState {
 // of the next one into the other buffer (nKV/nSc). The two buffers are distinct LDS
 // variables, so the compiler can tell the in-flight direct-to-LDS writes from the reads
 // of this block and need not wait for them before reading.
+// GUARD: a row may meet blocks before its first visible key (a key partition that
+// starts past the row's last key); its state then stays empty instead of taking NaNs.
+// Without key partitions every row sees key 0 in its first block.
+template <int GUARD>
 __device__ __forceinline__ void block_step(
     int kb, int nkb, const BlockLoader& ld, BlockLoader::Pages& pg_next, const RowCtx& rc,
     RowState& st, const int8_t* sK, const int8_t* sV, const float* sSk, const float* sSv,
@@ -193,14 +198,14 @@ __device__ __forceinline__ void block_step(
   const float xmax = ymax * rc.rs;
   if (__any(xmax > st.m_run + kLazyRescale)) {
     const float m_new = fmaxf(st.m_run, col_max(xmax));
-    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+    const float alpha = (GUARD && m_new == st.m_run) ? 1.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) st.acc[dt] *= alpha;
     st.l_part *= alpha;
     st.corr *= alpha;
     st.m_run = m_new;
   }
-  const float nm = -st.m_run;
+  const float nm = (GUARD && st.m_run == -INFINITY) ? 0.f : -st.m_run;
   float wm = 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -267,19 +272,41 @@ __device__ __forceinline__ void block_step(
 
 // Q8: the query arrives as int8 codes with fp32 scales (kv_produce's output) instead of
 // bf16 rows to quantize.
-template <int Q8>
+// SPLIT: the keys are cut into partitions of part_blocks 64-key blocks, one workgroup per
+// (KV head, partition, query block); each writes the partial softmax state (max, sum,
+// unnormalised output) of its rows over its partition, and the decode merge kernel
+// combines them.
+struct SplitOut {
+  float* ws_m;
+  float* ws_l;
+  float* ws_o;
+  int part_blocks;  // 64-key blocks per partition
+  int n_parts;
+};
+
+template <int Q8, int SPLIT>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
     const void* __restrict__ q, const float* __restrict__ q_scales, int n_new,
     const int8_t* __restrict__ k_cache,
     const int8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int ctx,
     int causal, int num_pages, int n_q_heads, int n_kv_heads, float qk_scale_log2,
-    float* __restrict__ out, int n_qb, int xcd_per_head) {
+    float* __restrict__ out, int n_qb, int xcd_per_head, SplitOut sp) {
   // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs (linear id
   // mod 8), so give each KV head its own XCDs (8 / H of them when H divides 8). Each
   // XCD's L2 then streams the K/V of one head instead of all of them.
-  int qb, g;
-  {
+  int qb, g, part = 0;
+  if (SPLIT) {
+    // Work items (KV head, partition, query block), query block fastest, dealt to the
+    // XCDs in 8 contiguous runs: the query blocks that read one partition share an L2.
+    const int total = n_kv_heads * sp.n_parts * n_qb;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int L = blockIdx.x, wi = (L % kXcds) * per + L / kXcds;
+    if (wi >= total) return;  // padding workgroup (whole block)
+    qb = wi % n_qb;
+    part = (wi / n_qb) % sp.n_parts;
+    g = wi / (n_qb * sp.n_parts);
+  } else {
     const int L = blockIdx.x, xcd = L % kXcds, slot = L / kXcds;
     if (xcd_per_head > 0) {
       g = xcd / xcd_per_head;
@@ -299,7 +326,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
   const int nq = min(kPfTok, n_new - t0);
   const int pos0 = ctx - n_new;
   const int kend = causal ? pos0 + t0 + nq : ctx;  // keys [0, kend) are needed
-  const int nkb = (kend + 63) >> 6;
+  // 64-key blocks [kb0, nkb) of this workgroup: all of them, or one partition's
+  const int kb0 = SPLIT ? part * sp.part_blocks : 0;
+  const int nkb = SPLIT ? min((kend + 63) >> 6, kb0 + sp.part_blocks) : (kend + 63) >> 6;
+  if (SPLIT && kb0 >= nkb) return;  // no row of this tile reaches the partition (whole block)
   const int my_tok = t0 + 16 * half + n;            // this lane's query token
 
   // Two K/V buffers and two scale buffers, each its own LDS variable.
@@ -312,9 +342,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
 
   const BlockLoader ld{k_cache, v_cache, k_scale, v_scale, block_table, (ctx + kPage - 1) / kPage,
                        num_pages, n_kv_heads, g, w, lane};
-  BlockLoader::Pages pg_next = ld.pages(0);
-  if (nkb > 0) ld.issue(pg_next, 0, s_kv0, s_sc0);  // first block in flight during the Q work
-  pg_next = ld.pages(1);
+  BlockLoader::Pages pg_next = ld.pages(kb0);
+  if (nkb > kb0) ld.issue(pg_next, kb0, s_kv0, s_sc0);  // first block in flight during the Q work
+  pg_next = ld.pages(kb0 + 1);
 
   // ---- quantize this wave's 16 query rows (head h); rows past the chunk are zero.
   int8_t* qrows = &s_q[hl * kPfTok + 16 * half][0];
@@ -368,15 +398,35 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) st.acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int kb = 0; kb < nkb; kb += 2) {
-    block_step(kb, nkb, ld, pg_next, rc, st, s_kv0[0], s_kv0[1], s_sc0[0], s_sc0[1], s_kv1, s_sc1);
+  for (int kb = kb0; kb < nkb; kb += 2) {
+    block_step<SPLIT>(kb, nkb, ld, pg_next, rc, st, s_kv0[0], s_kv0[1], s_sc0[0], s_sc0[1], s_kv1,
+                      s_sc1);
     if (kb + 1 < nkb)
-      block_step(kb + 1, nkb, ld, pg_next, rc, st, s_kv1[0], s_kv1[1], s_sc1[0], s_sc1[1], s_kv0,
-                 s_sc0);
+      block_step<SPLIT>(kb + 1, nkb, ld, pg_next, rc, st, s_kv1[0], s_kv1[1], s_sc1[0], s_sc1[1], s_kv0,
+                        s_sc0);
   }
 
   // ---- normalise and store: lane (n, gq) holds dims 16*dt + 4*gq + i of its row.
   const float l = col_sum(st.l_part);
+  if (SPLIT) {  // the partial state over this partition (rows without a key in it are
+                // never read by the merge)
+    if (my_tok < t0 + nq) {
+      const size_t pi = ((size_t)my_tok * n_q_heads + h) * sp.n_parts + part;
+      float* o = sp.ws_o + pi * kHeadDim + 4 * gq;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) {
+        float4 v;
+        v.x = st.acc[dt][0] - st.corr; v.y = st.acc[dt][1] - st.corr;
+        v.z = st.acc[dt][2] - st.corr; v.w = st.acc[dt][3] - st.corr;
+        *reinterpret_cast<float4*>(o + 16 * dt) = v;
+      }
+      if (gq == 0) {
+        sp.ws_m[pi] = st.m_run;
+        sp.ws_l[pi] = l;
+      }
+    }
+    return;
+  }
   if (my_tok < t0 + nq) {
     const float il = 1.0f / l;
     float* o = out + ((size_t)my_tok * n_q_heads + h) * kHeadDim + 4 * gq;
@@ -390,11 +440,17 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
   }
 }
 
+// Bytes of the partial states of np (row, head, partition) triples: o[256], m and l in
+// fp32, rounded up to 256.
+static size_t split_state_bytes(size_t np) {
+  return ((2 * np + np * kHeadDim) * sizeof(float) + 255) / 256 * 256;
+}
+
 int launch_prefill(const void* q, const float* q_scales, int n_new, const int8_t* k_cache,
                    const int8_t* v_cache,
                    const float* k_scale, const float* v_scale, const int32_t* block_table,
                    int ctx, int causal, int num_pages, int n_q_heads, int n_kv_heads,
-                   float sm_scale, float* out, hipStream_t stream) {
+                   float sm_scale, float* out, float* ws, size_t ws_bytes, hipStream_t stream) {
   const int n_qb = (n_new + kPfTok - 1) / kPfTok;
   // Heads spread over the XCDs when the head count divides their number; otherwise the
   // plain (head-major) order.
@@ -402,17 +458,71 @@ int launch_prefill(const void* q, const float* q_scales, int n_new, const int8_t
   const long long n_wg = xcd_per_head > 0
                              ? (long long)kXcds * ((n_qb + xcd_per_head - 1) / xcd_per_head)
                              : (long long)n_qb * n_kv_heads;
-  if (q_scales != nullptr)
-    hipLaunchKernelGGL(prefill_chunk_kernel<1>, dim3((unsigned)n_wg), dim3(kPfThreads), 0, stream,
-                       q, q_scales, n_new, k_cache, v_cache, k_scale, v_scale, block_table, ctx,
-                       causal, num_pages, n_q_heads, n_kv_heads, sm_scale * kLog2e, out, n_qb,
-                       xcd_per_head);
-  else
-    hipLaunchKernelGGL(prefill_chunk_kernel<0>, dim3((unsigned)n_wg), dim3(kPfThreads), 0, stream,
-                       q, q_scales, n_new, k_cache, v_cache, k_scale, v_scale, block_table, ctx,
-                       causal, num_pages, n_q_heads, n_kv_heads, sm_scale * kLog2e, out, n_qb,
-                       xcd_per_head);
-  return check_launch("attn_prefill_chunk");
+  SplitOut sp{nullptr, nullptr, nullptr, 0, 1};
+  const int n_parts = ws != nullptr ? prefill_split_parts(n_new, ctx, causal, n_kv_heads, &sp.part_blocks) : 1;
+  if (n_parts > 1) {
+    const size_t np = (size_t)n_new * n_q_heads * n_parts;
+    if (ws_bytes < prefill_split_ws_bytes(n_new, ctx, causal, n_q_heads, n_kv_heads))
+      return set_error(I8A_EWORKSPACE, "attn_prefill_chunk_split: workspace too small");
+    sp.ws_o = ws;  // [row][head][partition][256], then m and l
+    sp.ws_m = ws + np * kHeadDim;
+    sp.ws_l = sp.ws_m + np;
+    sp.n_parts = n_parts;
+    if (q_scales == nullptr) {
+      // bf16 rows: quantized once here (bit for bit the in-kernel quantizer) instead of by
+      // every partition's workgroup; the int8 codes and scales follow the partial states.
+      const size_t rows = (size_t)n_new * n_q_heads;
+      int8_t* codes = reinterpret_cast<int8_t*>(ws) + split_state_bytes(np);
+      float* scales = reinterpret_cast<float*>(codes + (rows * kHeadDim + 255) / 256 * 256);
+      int rc = launch_q_quant(static_cast<const uint16_t*>(q), (int)rows, codes, scales, stream);
+      if (rc) return rc;
+      q = codes;
+      q_scales = scales;
+    }
+  }
+  const dim3 grid(n_parts > 1 ? (unsigned)(kXcds * ((n_qb * n_kv_heads * n_parts + kXcds - 1) / kXcds))
+                              : (unsigned)n_wg);
+  const float qs = sm_scale * kLog2e;
+#define PF_ARGS q, q_scales, n_new, k_cache, v_cache, k_scale, v_scale, block_table, ctx, causal, \
+                num_pages, n_q_heads, n_kv_heads, qs, out, n_qb, xcd_per_head, sp
+  if (n_parts > 1) {  // (the query is int8 codes by now)
+    hipLaunchKernelGGL((prefill_chunk_kernel<1, 1>), grid, dim3(kPfThreads), 0, stream, PF_ARGS);
+  } else {
+    if (q_scales != nullptr)
+      hipLaunchKernelGGL((prefill_chunk_kernel<1, 0>), grid, dim3(kPfThreads), 0, stream, PF_ARGS);
+    else
+      hipLaunchKernelGGL((prefill_chunk_kernel<0, 0>), grid, dim3(kPfThreads), 0, stream, PF_ARGS);
+  }
+#undef PF_ARGS
+  int rc = check_launch("attn_prefill_chunk");
+  if (rc || n_parts == 1) return rc;
+  // Query row t of the chunk sees ctx - n_new + t + 1 keys: the merge of nq = n_new rows.
+  return launch_merge(sp.ws_m, sp.ws_l, sp.ws_o, nullptr, ctx, 1, n_new, n_q_heads, n_parts,
+                      sp.part_blocks * 64, out, stream);
+}
+
+// Partitions for a chunk whose single pass would leave most CUs idle: causal chunks with
+// fewer than 128 (query block, KV head) workgroups are cut into partitions of whole
+// 64-key blocks so that about 256 workgroups run. Returns 1 for the single pass.
+int prefill_split_parts(int n_new, int ctx, int causal, int n_kv_heads, int* part_blocks) {
+  const long long n_wg = (long long)((n_new + kPfTok - 1) / kPfTok) * n_kv_heads;
+  const int nkb = (ctx + 63) / 64;
+  *part_blocks = nkb;
+  if (!causal || n_wg <= 0 || n_wg >= 128 || nkb < 2) return 1;
+  int parts = (int)((256 + n_wg - 1) / n_wg);
+  parts = parts < nkb ? parts : nkb;
+  const int pb = (nkb + parts - 1) / parts;
+  *part_blocks = pb;
+  return (nkb + pb - 1) / pb;
+}
+
+size_t prefill_split_ws_bytes(int n_new, int ctx, int causal, int n_q_heads, int n_kv_heads) {
+  int pb;
+  const int parts = prefill_split_parts(n_new, ctx, causal, n_kv_heads, &pb);
+  if (parts <= 1) return 0;
+  const size_t rows = (size_t)n_new * n_q_heads;
+  return split_state_bytes(rows * parts) + (rows * kHeadDim + 255) / 256 * 256 +
+         (rows * sizeof(float) + 255) / 256 * 256;
 }
 
 }  // namespace i8a

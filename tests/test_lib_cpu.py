@@ -234,3 +234,53 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(TypeError):
         m.q_quant(torch.zeros(2, 256, dtype=torch.bfloat16))
+
+
+def test_attn_prefill_split_workspace_and_validation():
+    C = _codes()
+    L = m.lib()
+    wsb = m.attn_prefill_chunk_split_workspace_bytes
+    assert wsb(200, 1500, False, 24, 4) == 0      # non-causal: the one pass
+    assert wsb(1100, 5000, True, 24, 4) == 0      # 35 query blocks x 4 heads >= 128
+    assert wsb(10, 64, True, 24, 4) == 0          # a single 64-key block
+    assert wsb(0, 100, True, 24, 4) == 0
+    assert wsb(16, 100, True, 24, 5) == 0         # not a group of 6
+    up = lambda x: (x + 255) // 256 * 256
+
+    def expect(rows, parts):
+        # floats o[256], m and l per (row, head, partition), rounded up to 256 bytes; then
+        # the query codes and scales, each rounded up to 256 bytes.
+        return up(rows * parts * 258 * 4) + up(rows * 256) + up(rows * 4)
+
+    # 16 rows, 100 keys = two 64-key blocks: 4 workgroups ask for 64 partitions, capped
+    # at one block each = 2 partitions.
+    assert wsb(16, 100, True, 24, 4) == expect(16 * 24, 2)
+    # 12 rows at 20000 keys with one KV head: 256 partitions of 2 blocks -> 157 partitions
+    assert wsb(12, 20000, True, 6, 1) == expect(12 * 6, 157)
+    # At most 8 rows: the int8-P decode kernel's partials (m, l, o[256] per row, head and
+    # partition of 256 keys here: 1 x 1 x 79 partitions of 256 reach 64 workgroups).
+    assert wsb(3, 20000, True, 6, 1) == up(3 * 6 * 79 * 258 * 4)
+    assert wsb(8, 32768, True, 24, 4) == up(8 * 24 * 64 * 258 * 4)  # 512-key partitions
+
+    need = wsb(16, 100, True, 24, 4)
+    base = [FAKE, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 1, 16, 24, 4, 256, 0.0625, FAKE,
+            FAKE, need, None]
+
+    def call(i=None, val=None, fn=L.attn_prefill_chunk_split, args=base):
+        a = list(args)
+        if i is not None:
+            a[i] = val
+        return fn(*a)
+
+    assert call(16, need - 1) == C["I8A_EWORKSPACE"]
+    assert call(15, None) == C["I8A_EINVAL"]              # no workspace
+    assert call(15, FAKE + 4) == C["I8A_EINVAL"]          # not 16-byte aligned
+    assert call(8, 2) == C["I8A_EINVAL"]                  # causal flag
+    assert call(10, 12) == C["I8A_EUNSUPPORTED"]
+    assert call(1, 0) == C["I8A_OK"]                      # no queries: no-op
+    # A chunk that takes the one pass needs no workspace.
+    one = [FAKE, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 0, 16, 24, 4, 256, 0.0625, None,
+           None, 0, None]
+    assert call(fn=L.attn_prefill_chunk_split, args=one) == C["I8A_EINVAL"]  # (out null)
+    q8 = [FAKE, None] + base[1:]
+    assert call(fn=L.attn_prefill_chunk_split_q8, args=q8) == C["I8A_EINVAL"]  # no q_scales
