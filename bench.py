@@ -293,6 +293,25 @@ def main():
                       dtype=torch.uint8, device=dev)
     i8p_us = group_us(lambda c: lib.attn_decode_int8p(q_dec, c, table, ctx_t, ctx, out=out_dec,
                                                       workspace=ws8))
+    # short chunks at the end of the prefill context (the last n query rows): the split
+    # route (key partitions + merge, or the int8-P decode kernel for n <= 8) against the
+    # one pass; both stream the whole int8 K/V of the head group
+    short = {}
+    ws_sp = torch.empty(max(lib.attn_prefill_chunk_split_workspace_bytes(
+        256, pf.context_len, True, pf.n_q_heads, pf.n_kv_heads), 256), dtype=torch.uint8,
+        device=dev)
+    for n in (1, 16, 64, 256):
+        qn = q_pf[-n:]
+        on = torch.empty((n, pf.n_q_heads, pf.head_dim), dtype=torch.float32, device=dev)
+        t_split = group_us(lambda c: lib.attn_prefill_chunk_split(
+            qn, pcache, ptable, pf.context_len, True, out=on, workspace=ws_sp))
+        t_one = group_us(lambda c: lib.attn_prefill_chunk(qn, pcache, ptable, pf.context_len,
+                                                          True, out=on), reps=2)
+        ops = prefill_ops(pf.context_len, n, pf.n_q_heads, pf.head_dim)
+        kv_b = decode_bytes(pf.context_len, pf.n_q_heads, pf.n_kv_heads, pf.head_dim)
+        short[f"n{n}"] = {"split_us": round(t_split, 2), "one_pass_us": round(t_one, 1),
+                          "int8_TOPS": round(ops / (t_split * 1e-6) / 1e12, 1),
+                          "kv_GBps": round(kv_b / (t_split * 1e-6) / 1e9, 1)}
     # the fused producer (RoPE on Q/K, Q/K/V quantized, K/V paged write) for the chunk's
     # 2,048 tokens and for one decode token, bf16 inputs as a projection would give them
     qb = q_pf                                            # bf16 [2048, 24, 256]
@@ -358,6 +377,7 @@ def main():
     res["verify_ctx32768"] = verify
     res["decode_int8p_ctx32768"] = {"us": round(i8p_us, 3), "partition": part,
                                     "hbm_GBps": round(dec_b / (i8p_us * 1e-6) / 1e9, 1)}
+    res["prefill_short_chunks_ctx32768"] = short
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

@@ -155,16 +155,21 @@ int attn_chunk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
                     int causal, int n_q_heads, int n_kv_heads, int head_dim,
                     float sm_scale, float* out, void* stream);
 
-/* Bytes of scratch prefill_step needs: the larger of the rotated bf16 Q and K rows
- * (n_new * (n_q_heads + n_kv_heads) * head_dim * 2) and the int8 Q codes with scales
- * (n_new * n_q_heads * (head_dim + 4)), rounded up to 256. 0 for invalid arguments. */
-size_t prefill_step_workspace_bytes(int n_new, int n_q_heads, int n_kv_heads, int head_dim);
+/* Bytes of scratch prefill_step needs for a chunk of n_new rows ending at context_len:
+ * without history (context_len == n_new) the rotated bf16 Q and K rows
+ * (n_new * (n_q_heads + n_kv_heads) * head_dim * 2, rounded up to 256); with history the
+ * int8 Q codes with scales (n_new * n_q_heads * (head_dim + 4), rounded up to 256) plus
+ * attn_prefill_chunk_split_workspace_bytes(n_new, context_len, 1, ...). 0 for invalid
+ * arguments. */
+size_t prefill_step_workspace_bytes(int n_new, int context_len, int n_q_heads, int n_kv_heads,
+                                    int head_dim);
 
 /* prefill_step -- one prefill chunk end to end, routed by its history [DCU §3.1, §3.2]:
  * the producer (RoPE, quantization, paged K/V write) runs first, then
  *  - context_len == n_new (no history): attn_chunk_bf16 on the rotated bf16 rows;
- *  - otherwise: attn_prefill_chunk_q8 on the int8 cache with the producer's Q codes
- *    (the history exists only as int8).
+ *  - otherwise: attn_prefill_chunk_split_q8 on the int8 cache with the producer's Q
+ *    codes (the history exists only as int8; short chunks split over key partitions,
+ *    the others in one pass).
  *  q, k, v       bf16 [n_new][heads][head_dim] as projected (before RoPE).
  *  positions, cos_sin, rotary_dim, max_position, slot_mapping, caches: as for kv_produce.
  *  block_table, context_len: as for attn_prefill_chunk (context_len counts the chunk).
@@ -347,12 +352,16 @@ int attn_prefill_chunk(const uint16_t* q, int n_new,
  *                attn_prefill_chunk_split_workspace_bytes(...) bytes; its contents on
  *                entry do not matter and are overwritten. Calls that share a workspace
  *                must be ordered (same stream).
- *  The route: a causal chunk with fewer than 128 (32-token query block, KV head) pairs
- *  is cut into partitions of whole 64-key blocks so that about 256 workgroups run, and
- *  a second kernel merges the partitions; any other chunk (and every non-causal one)
- *  takes the one pass of attn_prefill_chunk, bit for bit, and needs no workspace. The
- *  int8 weight codes are per aligned 64-key block in both routes, so the split result
- *  differs from the one pass only by rounding in the merge.
+ *  The route, for causal chunks:
+ *  - n_new <= 8: the int8-P decode kernel (attn_decode_int8p with nq = n_new and its
+ *    default partitions; bit for bit its result), which reads each K/V tile once for
+ *    all rows of a KV head;
+ *  - fewer than 128 (32-token query block, KV head) pairs: the chunk kernel over key
+ *    partitions of whole 64-key blocks, about 256 workgroups, then a merge kernel (bf16
+ *    queries are first quantized once, as q_quant does);
+ *  - otherwise: the one pass of attn_prefill_chunk, bit for bit, with no workspace.
+ *  Non-causal chunks always take the one pass. The int8 weight codes are per aligned
+ *  64-key block in every route, so the routes differ only by rounding in the merge.
  *  workspace_bytes below the required size returns I8A_EWORKSPACE. */
 size_t attn_prefill_chunk_split_workspace_bytes(int n_new, int context_len, int causal,
                                                 int n_q_heads, int n_kv_heads, int head_dim);

@@ -52,7 +52,7 @@ _SIGNATURES = {
                             _c_void, _c_int, _c_void, _c_void, _c_void, _c_void, _c_void]),
     "attn_chunk_bf16": (_c_int, [_c_void, _c_void, _c_void, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _c_float, _c_void, _c_void]),
-    "prefill_step_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
+    "prefill_step_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "prefill_step": (_c_int, [_c_void, _c_void, _c_void, _c_int, _c_void, _c_void, _c_int, _c_int,
                               _c_void, _c_void, _c_void, _c_void, _c_void, _c_int, _c_void, _c_int,
                               _c_int, _c_int, _c_int, _c_float, _c_void, _c_void, _c_size,
@@ -264,9 +264,10 @@ def attn_chunk_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: b
     return out
 
 
-def prefill_step_workspace_bytes(n_new: int, n_q_heads: int, n_kv_heads: int,
+def prefill_step_workspace_bytes(n_new: int, context_len: int, n_q_heads: int, n_kv_heads: int,
                                  head_dim: int = HEAD_DIM) -> int:
-    return int(lib().prefill_step_workspace_bytes(n_new, n_q_heads, n_kv_heads, head_dim))
+    return int(lib().prefill_step_workspace_bytes(n_new, context_len, n_q_heads, n_kv_heads,
+                                                  head_dim))
 
 
 def prefill_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
@@ -282,7 +283,7 @@ def prefill_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: t
     n_new, Hq, D = q.shape
     if out is None:
         out = torch.empty((n_new, Hq, D), dtype=torch.float32, device=q.device)
-    need = prefill_step_workspace_bytes(n_new, Hq, cache.n_kv_heads, D)
+    need = prefill_step_workspace_bytes(n_new, int(context_len), Hq, cache.n_kv_heads, D)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     sm = float(sm_scale if sm_scale is not None else D ** -0.5)

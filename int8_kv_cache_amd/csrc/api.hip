@@ -143,12 +143,24 @@ int attn_chunk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
                            (hipStream_t)stream);
 }
 
-size_t prefill_step_workspace_bytes(int n_new, int n_q_heads, int n_kv_heads, int head_dim) {
-  if (n_new <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim != 256) return 0;
-  const size_t rot = (size_t)n_new * (n_q_heads + n_kv_heads) * head_dim * 2;  // bf16 Q, K
-  const size_t q8 = (size_t)n_new * n_q_heads * (head_dim + 4);               // codes + scales
-  const size_t need = rot > q8 ? rot : q8;
-  return (need + 255) / 256 * 256;
+// The int8 route's Q codes and scales, rounded up to 256 bytes; its split-route scratch
+// follows them.
+static size_t step_q8_bytes(int n_new, int n_q_heads) {
+  return ((size_t)n_new * n_q_heads * (256 + 4) + 255) / 256 * 256;
+}
+
+size_t prefill_step_workspace_bytes(int n_new, int context_len, int n_q_heads, int n_kv_heads,
+                                    int head_dim) {
+  if (n_new <= 0 || context_len < n_new || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim != 256 ||
+      n_q_heads != 6 * n_kv_heads)
+    return 0;
+  if (context_len == n_new) {  // bf16 route: the rotated Q and K rows
+    const size_t rot = (size_t)n_new * (n_q_heads + n_kv_heads) * head_dim * 2;
+    return (rot + 255) / 256 * 256;
+  }
+  return step_q8_bytes(n_new, n_q_heads) +
+         attn_prefill_chunk_split_workspace_bytes(n_new, context_len, 1, n_q_heads, n_kv_heads,
+                                                  head_dim);
 }
 
 int prefill_step(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n_new,
@@ -164,7 +176,7 @@ int prefill_step(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n_
   if (n_new == 0) return I8A_OK;
   if (!workspace || ((uintptr_t)workspace & 255u) != 0)
     return set_error(I8A_EINVAL, "prefill_step: workspace null or not 256-byte aligned");
-  const size_t need = prefill_step_workspace_bytes(n_new, n_q_heads, n_kv_heads, head_dim);
+  const size_t need = prefill_step_workspace_bytes(n_new, context_len, n_q_heads, n_kv_heads, head_dim);
   if (workspace_bytes < need)
     return set_error(I8A_EWORKSPACE, "prefill_step: workspace %zu bytes < %zu needed", workspace_bytes, need);
   char* ws = static_cast<char*>(workspace);
@@ -180,16 +192,19 @@ int prefill_step(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n_
     return attn_chunk_bf16(q_rot, k_rot, v, n_new, 1, n_q_heads, n_kv_heads, head_dim, sm_scale,
                            out, stream);
   }
-  // A history exists (in the int8 cache only): the int8 chunk path with the producer's Q.
+  // A history exists (in the int8 cache only): the int8 chunk path with the producer's Q,
+  // split over key partitions when the chunk is short.
   int8_t* q_codes = reinterpret_cast<int8_t*>(ws);
   float* q_scales = reinterpret_cast<float*>(ws + (size_t)n_new * n_q_heads * head_dim);
   rc = kv_produce(q, k, v, I8A_DTYPE_BF16, n_new, n_q_heads, n_kv_heads, head_dim, positions,
                   cos_sin, rotary_dim, max_position, slot_mapping, k_cache, v_cache, k_scale,
                   v_scale, num_pages, q_codes, q_scales, nullptr, nullptr, stream);
   if (rc) return rc;
-  return attn_prefill_chunk_q8(q_codes, q_scales, n_new, k_cache, v_cache, k_scale, v_scale,
-                               block_table, context_len, 1, num_pages, n_q_heads, n_kv_heads,
-                               head_dim, sm_scale, out, stream);
+  const size_t q8 = step_q8_bytes(n_new, n_q_heads);
+  return attn_prefill_chunk_split_q8(q_codes, q_scales, n_new, k_cache, v_cache, k_scale, v_scale,
+                                     block_table, context_len, 1, num_pages, n_q_heads,
+                                     n_kv_heads, head_dim, sm_scale, out, ws + q8,
+                                     workspace_bytes - q8, stream);
 }
 
 int q_quant(const uint16_t* q_bf16, int n_rows, int head_dim, int8_t* codes, float* scales,

@@ -87,16 +87,18 @@ def test_producer_rotated_rows_bit_exact():
 
 def test_prefill_step_routes_by_history():
     need_gpu()
-    say("prefill_step: 300-token first chunk (bf16 route), then 100 tokens (int8 route)")
-    full = workloads.make_producer_case(220, 400, start=0, rotary_dim=256)
+    say("prefill_step: 300-token first chunk (bf16 route), then 100 tokens (int8 route, key "
+        "partitions), then 5 tokens (int8 route, int8-P decode kernel)")
+    full = workloads.make_producer_case(220, 405, start=0, rotary_dim=256)
     q, k, v = full.data()
     qb, kb, vb = (workloads.f32_to_bf16_bits(a) for a in (q, k, v))
     q, k, v = (quant.bf16_bits_to_f32(a) for a in (qb, kb, vb))
     table = full.table()
     cache = gpu_cache(full.num_pages, 4)
     block_row = up((full.slots[::16] // 16).astype(np.int32))
+    chunks = ((0, 300), (300, 400), (400, 405))
     outs = []
-    for a, b in ((0, 300), (300, 400)):
+    for a, b in chunks:
         sl = slice(a, b)
         outs.append(lib.prefill_step(_bf16(qb[sl]), _bf16(kb[sl]), _bf16(vb[sl]),
                                      up(full.positions[sl]), up(table), up(full.slots[sl]), cache,
@@ -112,19 +114,20 @@ def test_prefill_step_routes_by_history():
     e1 = float(np.max(np.abs(outs[0].cpu().numpy() - ref1)))
     say(f"  first chunk: err {e1:.3e} (bound {TOL * vmax:.3e})")
     assert e1 <= TOL * vmax
-    # second chunk: the int8 path over the whole int8 cache with the producer's Q codes
-    qc, qs = rope.produce(q[300:], k[300:], v[300:], full.positions[300:], table, 256,
-                          full.slots[300:], ref_cache)
+    # later chunks: the int8 path over the int8 cache with the producer's Q codes
+    for (a, b), o in zip(chunks[1:], outs[1:]):
+        qc, qs = rope.produce(q[a:b], k[a:b], v[a:b], full.positions[a:b], table, 256,
+                              full.slots[a:b], ref_cache)
+        kc, ks, vc, vs = paged.gather_seq(ref_cache, full.slots[::16] // 16, b, 4)
+        qd2 = quant.dequantize(qc, qs)
+        last = a + np.arange(b - a)
+        ref_a = attention.attention_exact(qd2, quant.dequantize(kc, ks), quant.dequantize(vc, vs),
+                                          1 / 16, last)
+        ref_b = attention.attention_int8p(qd2, quant.dequantize(kc, ks), vc, vs, 1 / 16, last)
+        vmax2 = float(np.max(np.abs(quant.dequantize(vc, vs))))
+        o2 = o.cpu().numpy()
+        ea, eb = float(np.max(np.abs(o2 - ref_a))), float(np.max(np.abs(o2 - ref_b)))
+        say(f"  chunk {a}..{b}: err vs exact {ea:.3e}, vs int8-P rule {eb:.3e} (max|V| {vmax2:.3f})")
+        assert ea <= 1e-2 * vmax2 and eb <= 1e-3 * vmax2
     for a_, b_ in zip(cache_to_host(cache), ref_cache):
         assert np.array_equal(a_, b_)
-    view = paged.gather_seq(ref_cache, full.slots[::16] // 16, 400, 4)
-    kc, ks, vc, vs = view
-    qd2 = quant.dequantize(qc, qs)
-    last = 300 + np.arange(100)
-    ref_a = attention.attention_exact(qd2, quant.dequantize(kc, ks), quant.dequantize(vc, vs), 1 / 16, last)
-    ref_b = attention.attention_int8p(qd2, quant.dequantize(kc, ks), vc, vs, 1 / 16, last)
-    vmax2 = float(np.max(np.abs(quant.dequantize(vc, vs))))
-    o2 = outs[1].cpu().numpy()
-    ea, eb = float(np.max(np.abs(o2 - ref_a))), float(np.max(np.abs(o2 - ref_b)))
-    say(f"  second chunk: err vs exact {ea:.3e}, vs int8-P rule {eb:.3e} (max|V| {vmax2:.3f})")
-    assert ea <= 1e-2 * vmax2 and eb <= 1e-3 * vmax2

@@ -198,8 +198,12 @@ def test_kv_produce_and_q8_validation():
     assert call(0, None) == C["I8A_EINVAL"]             # q_codes without q
     cb = [FAKE, FAKE, FAKE, 64, 2, 24, 4, 256, 0.0625, FAKE, None]
     assert L.attn_chunk_bf16(*cb) == C["I8A_EINVAL"]    # causal flag
-    ps = m.prefill_step_workspace_bytes(100, 24, 4)
+    ps = m.prefill_step_workspace_bytes(100, 100, 24, 4)   # no history: rotated bf16 Q, K
     assert ps == (100 * 28 * 256 * 2 + 255) // 256 * 256
+    q8 = (100 * 24 * 260 + 255) // 256 * 256               # history: Q codes + split scratch
+    assert m.prefill_step_workspace_bytes(100, 5000, 24, 4) == \
+        q8 + m.attn_prefill_chunk_split_workspace_bytes(100, 5000, True, 24, 4)
+    assert m.prefill_step_workspace_bytes(2048, 32768, 24, 4) == (2048 * 24 * 260 + 255) // 256 * 256
     step = [FAKE, FAKE, FAKE, 100, FAKE, FAKE, 64, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, 50, FAKE,
             100, 24, 4, 256, 0.0625, FAKE, 4096, ps - 1, None]
     assert L.prefill_step(*step) == C["I8A_EWORKSPACE"]
