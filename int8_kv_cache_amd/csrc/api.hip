@@ -35,7 +35,7 @@ static int check_heads(int n_q_heads, int n_kv_heads, int head_dim) {
   // The merge kernels put the query heads on grid.y (at most 65535).
   if (n_q_heads > 65535) return set_error(I8A_EINVAL, "n_q_heads %d > 65535", n_q_heads);
   if (head_dim != 256) return set_error(I8A_EUNSUPPORTED, "head_dim %d unsupported (v1: 256)", head_dim);
-  if (n_q_heads != 6 * n_kv_heads)
+  if (n_kv_heads > 65535 / 6 || n_q_heads != 6 * n_kv_heads)
     return set_error(I8A_EUNSUPPORTED, "n_q_heads %d / n_kv_heads %d: v1 supports GQA groups of 6",
                      n_q_heads, n_kv_heads);
   return I8A_OK;
@@ -151,8 +151,8 @@ static size_t step_q8_bytes(int n_new, int n_q_heads) {
 
 size_t prefill_step_workspace_bytes(int n_new, int context_len, int n_q_heads, int n_kv_heads,
                                     int head_dim) {
-  if (n_new <= 0 || context_len < n_new || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim != 256 ||
-      n_q_heads != 6 * n_kv_heads)
+  if (n_new <= 0 || context_len < n_new || context_len > 2147483000 - 64 || n_q_heads <= 0 ||
+      n_kv_heads <= 0 || n_kv_heads > 65535 / 6 || head_dim != 256 || n_q_heads != 6 * n_kv_heads)
     return 0;
   if (context_len == n_new) {  // bf16 route: the rotated Q and K rows
     const size_t rot = (size_t)n_new * (n_q_heads + n_kv_heads) * head_dim * 2;
@@ -452,6 +452,7 @@ static int prefill_impl(const void* q, const float* q_scales, int n_new, const i
       (causal != 0 && causal != 1))
     return set_error(I8A_EINVAL, "attn_prefill_chunk: n_new %d, context_len %d, num_pages %d, causal %d",
                      n_new, context_len, num_pages, causal);
+  if (context_len > 2147483000 - 64) return set_error(I8A_EINVAL, "attn_prefill_chunk: context too long");
   size_t need = 0;
   if (split) {
     need = split_ws_bytes(n_new, context_len, causal, n_q_heads, n_kv_heads);
@@ -461,7 +462,6 @@ static int prefill_impl(const void* q, const float* q_scales, int n_new, const i
       return set_error(I8A_EWORKSPACE, "attn_prefill_chunk_split: workspace %zu bytes < %zu needed",
                        workspace_bytes, need);
   }
-  if (context_len > 2147483000 - 64) return set_error(I8A_EINVAL, "attn_prefill_chunk: context too long");
   if ((long long)num_pages * n_kv_heads * 16 >= (1ll << 32))
     return set_error(I8A_EUNSUPPORTED, "attn_prefill_chunk: num_pages %d x %d heads exceeds the scale index range",
                      num_pages, n_kv_heads);
@@ -503,8 +503,9 @@ int attn_prefill_chunk_q8(const int8_t* q_codes, const float* q_scales, int n_ne
 
 size_t attn_prefill_chunk_split_workspace_bytes(int n_new, int context_len, int causal,
                                                 int n_q_heads, int n_kv_heads, int head_dim) {
-  if (n_new <= 0 || context_len < n_new || (causal != 0 && causal != 1) || head_dim != 256 ||
-      n_kv_heads <= 0 || n_q_heads != n_kv_heads * 6)
+  if (n_new <= 0 || context_len < n_new || context_len > 2147483000 - 64 ||
+      (causal != 0 && causal != 1) || head_dim != 256 || n_kv_heads <= 0 ||
+      n_kv_heads > 65535 / 6 || n_q_heads != n_kv_heads * 6)
     return 0;
   return split_ws_bytes(n_new, context_len, causal, n_q_heads, n_kv_heads);
 }

@@ -506,7 +506,7 @@ int launch_prefill(const void* q, const float* q_scales, int n_new, const int8_t
 // 64-key blocks so that about 256 workgroups run. Returns 1 for the single pass.
 int prefill_split_parts(int n_new, int ctx, int causal, int n_kv_heads, int* part_blocks) {
   const long long n_wg = (long long)((n_new + kPfTok - 1) / kPfTok) * n_kv_heads;
-  const int nkb = (ctx + 63) / 64;
+  const int nkb = (int)(((long long)ctx + 63) / 64);
   *part_blocks = nkb;
   if (!causal || n_wg <= 0 || n_wg >= 128 || nkb < 2) return 1;
   int parts = (int)((256 + n_wg - 1) / n_wg);

@@ -226,6 +226,7 @@ def test_attn_prefill_validation():
         return L.attn_prefill_chunk(*a)
 
     assert call(10, 12) == C["I8A_EUNSUPPORTED"]
+    assert call(11, 2**30) == C["I8A_EUNSUPPORTED"]    # 6 x n_kv_heads would overflow
     assert call(1, 101) == C["I8A_EINVAL"]             # n_new > context_len
     assert call(8, 2) == C["I8A_EINVAL"]               # causal flag
     assert call(7, 0) == C["I8A_EINVAL"]               # empty context
@@ -249,6 +250,9 @@ def test_attn_prefill_split_workspace_and_validation():
     assert wsb(10, 64, True, 24, 4) == 0          # a single 64-key block
     assert wsb(0, 100, True, 24, 4) == 0
     assert wsb(16, 100, True, 24, 5) == 0         # not a group of 6
+    assert wsb(16, 2**31 - 1, True, 24, 4) == 0   # context past the supported range
+    assert wsb(16, 100, True, 24, 2**30) == 0     # head counts that would overflow
+    assert m.prefill_step_workspace_bytes(16, 2**31 - 1, 24, 4) == 0
     up = lambda x: (x + 255) // 256 * 256
 
     def expect(rows, parts):
