@@ -378,6 +378,62 @@ def main():
     res["decode_int8p_ctx32768"] = {"us": round(i8p_us, 3), "partition": part,
                                     "hbm_GBps": round(dec_b / (i8p_us * 1e-6) / 1e9, 1)}
     res["prefill_short_chunks_ctx32768"] = short
+    # ---- spread of the per-step event times, MALL-warm and graph-replayed decode, and
+    # ceilings measured on this machine (a 1 GiB device copy; hipBLASLt's int8 GEMM)
+    dec_steps = [events[i][3].elapsed_time(events[i][4]) * 1e3 / R
+                 for i in range(args.warmup, steps_total)]
+    pf_steps = [events[i][1].elapsed_time(events[i][2]) for i in range(args.warmup, steps_total)]
+    res["decode_us_spread"] = {"median": round(float(np.median(dec_steps)), 3),
+                               "min": round(min(dec_steps), 3), "max": round(max(dec_steps), 3)}
+    res["prefill_ms_spread"] = {"median": round(float(np.median(pf_steps)), 4),
+                                "min": round(min(pf_steps), 4), "max": round(max(pf_steps), 4)}
+
+    def per_call_us(fn, calls, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * calls)
+
+    def warm8():
+        for _ in range(R):
+            lib.attn_decode(q_dec, base, table, ctx_t, ctx, out=out_dec, workspace=ws)
+    warm_us = per_call_us(warm8, R)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in copies:
+            lib.attn_decode(q_dec, c, table, ctx_t, ctx, out=out_dec, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    dgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(dgraph):
+        for c in copies:
+            lib.attn_decode(q_dec, c, table, ctx_t, ctx, out=out_dec, workspace=ws)
+    graph_us = per_call_us(dgraph.replay, R)
+    res["decode_us_mall_warm"] = round(warm_us, 3)
+    res["decode_us_graph"] = round(graph_us, 3)
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    copy_GBps = 2 * nb / (per_call_us(lambda: dst.copy_(src), 1, reps=5) * 1e-6) / 1e9
+    del src, dst
+    try:
+        ga = torch.randint(-127, 128, (8192, 8192), dtype=torch.int8, device=dev)
+        gb = torch.randint(-127, 128, (8192, 8192), dtype=torch.int8, device=dev)
+        gemm_TOPS = 2 * 8192 ** 3 / (per_call_us(lambda: torch._int_mm(ga, gb), 1, reps=5) * 1e-6) / 1e12
+        del ga, gb
+    except (RuntimeError, AttributeError):
+        gemm_TOPS = None
+    res["measured_ceilings"] = {
+        "device_copy_GBps": round(copy_GBps, 1),
+        "decode_frac_of_copy": round(dec_gbps / copy_GBps, 4),
+        "int8_gemm_TOPS": None if gemm_TOPS is None else round(gemm_TOPS, 1),
+        "prefill_frac_of_int8_gemm": None if gemm_TOPS is None else round(pf_tops / gemm_TOPS, 4)}
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
