@@ -150,14 +150,29 @@ int kv_produce(const void* q, const void* k, const void* v, int in_dtype,
  *  multiply V as two bf16 terms (16 significant bits) with fp32 accumulation, so the
  *  output meets the fp32-class bound (1e-4 * max|V|) against exact attention on the
  *  same bf16 rows.
- *  out           fp32 [n][n_q_heads][head_dim]. n == 0 is a no-op. */
+ *  out           fp32 [n][n_q_heads][head_dim]. n == 0 is a no-op.
+ *  workspace     NULL: one pass, one workgroup per 32 query rows and KV head (the
+ *                causal tiles then run 1 .. n/64 key blocks each, and the longest sets
+ *                the time). Otherwise device scratch, 16-byte aligned, of at least
+ *                attn_chunk_bf16_workspace_bytes(...) bytes (contents on entry do not
+ *                matter): a causal chunk whose tiles reach past one key partition is
+ *                cut into partitions of the average work per CU, the tiles with most
+ *                keys first, and the rows past the first partition are merged by a
+ *                second kernel (log-sum-exp merge of the partial states, as in the
+ *                decode [DCU §3.3]). The two routes differ only by the merge's
+ *                rounding, within the same bound. A smaller workspace_bytes returns
+ *                I8A_EWORKSPACE. */
+size_t attn_chunk_bf16_workspace_bytes(int n, int causal, int n_q_heads, int n_kv_heads,
+                                       int head_dim);
 int attn_chunk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n,
                     int causal, int n_q_heads, int n_kv_heads, int head_dim,
-                    float sm_scale, float* out, void* stream);
+                    float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /* Bytes of scratch prefill_step needs for a chunk of n_new rows ending at context_len:
  * without history (context_len == n_new) the rotated bf16 Q and K rows
- * (n_new * (n_q_heads + n_kv_heads) * head_dim * 2, rounded up to 256); with history the
+ * (n_new * (n_q_heads + n_kv_heads) * head_dim * 2, rounded up to 256) plus
+ * attn_chunk_bf16_workspace_bytes(n_new, 1, ...); with history the
  * int8 Q codes with scales (n_new * n_q_heads * (head_dim + 4), rounded up to 256) plus
  * attn_prefill_chunk_split_workspace_bytes(n_new, context_len, 1, ...). 0 for invalid
  * arguments. */

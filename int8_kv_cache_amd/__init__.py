@@ -19,7 +19,8 @@ __all__ = ["lib", "PagedCache", "alloc_cache", "kv_quant_write", "q_quant", "att
            "attn_decode_workspace_bytes", "attn_verify", "attn_verify_workspace_bytes",
            "attn_decode_int8p", "attn_decode_int8p_workspace_bytes", "attn_decode_partition_rows",
            "attn_prefill_chunk", "attn_prefill_chunk_split",
-           "attn_prefill_chunk_split_workspace_bytes", "kv_produce", "attn_chunk_bf16", "prefill_step",
+           "attn_prefill_chunk_split_workspace_bytes", "kv_produce", "attn_chunk_bf16",
+           "attn_chunk_bf16_workspace_bytes", "prefill_step",
            "prefill_step_workspace_bytes", "Int8AttnError",
            "HEAD_DIM", "PAGE", "PARTITION", "EXPORTED_SYMBOLS"]
 
@@ -35,7 +36,8 @@ EXPORTED_SYMBOLS = ("int8attn_last_error", "int8attn_version", "kv_quant_write",
                     "attn_verify", "attn_decode_partition_rows",
                     "attn_decode_int8p_workspace_bytes", "attn_decode_int8p",
                     "attn_prefill_chunk", "attn_prefill_chunk_split_workspace_bytes",
-                    "attn_prefill_chunk_split", "attn_prefill_chunk_split_q8")
+                    "attn_prefill_chunk_split", "attn_prefill_chunk_split_q8",
+                    "attn_chunk_bf16_workspace_bytes")
 
 _c_void = ctypes.c_void_p
 _c_int = ctypes.c_int
@@ -51,7 +53,8 @@ _SIGNATURES = {
                             _c_void, _c_void, _c_int, _c_int, _c_void, _c_void, _c_void, _c_void,
                             _c_void, _c_int, _c_void, _c_void, _c_void, _c_void, _c_void]),
     "attn_chunk_bf16": (_c_int, [_c_void, _c_void, _c_void, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                 _c_float, _c_void, _c_void]),
+                                 _c_float, _c_void, _c_void, _c_size, _c_void]),
+    "attn_chunk_bf16_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "prefill_step_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "prefill_step": (_c_int, [_c_void, _c_void, _c_void, _c_int, _c_void, _c_void, _c_int, _c_int,
                               _c_void, _c_void, _c_void, _c_void, _c_void, _c_int, _c_void, _c_int,
@@ -244,11 +247,19 @@ def kv_produce(q, k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
     return (qr, kr) if rotated_bf16 else (codes, scales)
 
 
+def attn_chunk_bf16_workspace_bytes(n: int, causal: bool, n_q_heads: int, n_kv_heads: int,
+                                    head_dim: int = HEAD_DIM) -> int:
+    return int(lib().attn_chunk_bf16_workspace_bytes(n, int(bool(causal)), n_q_heads, n_kv_heads,
+                                                     head_dim))
+
+
 def attn_chunk_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
                     sm_scale: float | None = None, out: torch.Tensor | None = None,
-                    stream=None) -> torch.Tensor:
+                    stream=None, workspace: torch.Tensor | None = None,
+                    split: bool = True) -> torch.Tensor:
     """High-precision attention of a chunk over its own bf16 rows: q [n, Hq, 256],
-    k/v [n, Hkv, 256] -> out fp32 [n, Hq, 256]."""
+    k/v [n, Hkv, 256] -> out fp32 [n, Hq, 256]. split: key partitions for causal chunks
+    (a workspace is allocated when none is given); False: the one pass."""
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         if t.dtype != torch.bfloat16 or t.dim() != 3:
             raise TypeError(f"{nm} must be bfloat16 [n, heads, head_dim]")
@@ -258,9 +269,15 @@ def attn_chunk_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: b
     if out is None:
         out = torch.empty((n, Hq, D), dtype=torch.float32, device=q.device)
     sm = float(sm_scale if sm_scale is not None else D ** -0.5)
+    ws_ptr, ws_bytes = None, 0
+    if split:
+        if workspace is None:
+            need = attn_chunk_bf16_workspace_bytes(n, causal, Hq, k.shape[1], D)
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     _check(lib().attn_chunk_bf16(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), n, int(bool(causal)),
                                  Hq, k.shape[1], D, sm, _dev(out, "out", torch.float32),
-                                 _stream(stream)))
+                                 ws_ptr, ws_bytes, _stream(stream)))
     return out
 
 

@@ -129,17 +129,35 @@ int kv_produce(const void* q, const void* k, const void* v, int in_dtype, int n_
                            q_scales, q_rot, k_rot, (hipStream_t)stream);
 }
 
+size_t attn_chunk_bf16_workspace_bytes(int n, int causal, int n_q_heads, int n_kv_heads,
+                                       int head_dim) {
+  if (n <= 0 || (causal != 0 && causal != 1) || head_dim != 256 || n_kv_heads <= 0 ||
+      n_kv_heads > 65535 / 6 || n_q_heads != 6 * n_kv_heads || (long long)n * n_q_heads > 2147483000LL)
+    return 0;
+  return chunk_bf16_ws_bytes(n, causal, n_q_heads, n_kv_heads);
+}
+
 int attn_chunk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n, int causal,
                     int n_q_heads, int n_kv_heads, int head_dim, float sm_scale, float* out,
-                    void* stream) {
+                    void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
   if (rc) return rc;
   if (n < 0 || (causal != 0 && causal != 1) || (long long)n * n_q_heads > 2147483000LL)
     return set_error(I8A_EINVAL, "attn_chunk_bf16: n %d, causal %d", n, causal);
   if (!isfinite(sm_scale)) return set_error(I8A_EINVAL, "attn_chunk_bf16: sm_scale not finite");
+  size_t need = 0;
+  if (workspace != nullptr) {
+    if (((uintptr_t)workspace & 15u) != 0)
+      return set_error(I8A_EINVAL, "attn_chunk_bf16: workspace not 16-byte aligned");
+    need = n > 0 ? chunk_bf16_ws_bytes(n, causal, n_q_heads, n_kv_heads) : 0;
+    if (workspace_bytes < need)
+      return set_error(I8A_EWORKSPACE, "attn_chunk_bf16: workspace %zu bytes < %zu needed",
+                       workspace_bytes, need);
+  }
   if (n == 0) return I8A_OK;
   if (!q || !k || !v || !out) return set_error(I8A_EINVAL, "attn_chunk_bf16: null pointer");
   return launch_chunk_bf16(q, k, v, n, causal, n_q_heads, n_kv_heads, sm_scale, out,
+                           need > 0 ? static_cast<float*>(workspace) : nullptr,
                            (hipStream_t)stream);
 }
 
@@ -154,9 +172,10 @@ size_t prefill_step_workspace_bytes(int n_new, int context_len, int n_q_heads, i
   if (n_new <= 0 || context_len < n_new || context_len > 2147483000 - 64 || n_q_heads <= 0 ||
       n_kv_heads <= 0 || n_kv_heads > 65535 / 6 || head_dim != 256 || n_q_heads != 6 * n_kv_heads)
     return 0;
-  if (context_len == n_new) {  // bf16 route: the rotated Q and K rows
+  if (context_len == n_new) {  // bf16 route: the rotated Q and K rows, then the split scratch
     const size_t rot = (size_t)n_new * (n_q_heads + n_kv_heads) * head_dim * 2;
-    return (rot + 255) / 256 * 256;
+    return (rot + 255) / 256 * 256 +
+           attn_chunk_bf16_workspace_bytes(n_new, 1, n_q_heads, n_kv_heads, head_dim);
   }
   return step_q8_bytes(n_new, n_q_heads) +
          attn_prefill_chunk_split_workspace_bytes(n_new, context_len, 1, n_q_heads, n_kv_heads,
@@ -189,8 +208,9 @@ int prefill_step(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n_
                     cos_sin, rotary_dim, max_position, slot_mapping, k_cache, v_cache, k_scale,
                     v_scale, num_pages, nullptr, nullptr, q_rot, k_rot, stream);
     if (rc) return rc;
+    const size_t rot = ((size_t)n_new * (n_q_heads + n_kv_heads) * head_dim * 2 + 255) / 256 * 256;
     return attn_chunk_bf16(q_rot, k_rot, v, n_new, 1, n_q_heads, n_kv_heads, head_dim, sm_scale,
-                           out, stream);
+                           out, ws + rot, workspace_bytes - rot, stream);
   }
   // A history exists (in the int8 cache only): the int8 chunk path with the producer's Q,
   // split over key partitions when the chunk is short.

@@ -21,6 +21,8 @@
 //    key 16(2h + j/4) + 4 kg + j%4), so P needs no lane movement; V is staged as key rows
 //    by direct-to-LDS loads and read with gfx950's transposing LDS read (ds_read_b64_tr_b16),
 //    two per operand.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -182,12 +184,32 @@ __device__ __forceinline__ void block_step(int kb, int nkb, const Loader& ld, co
   lds_barrier();
 }
 
+// Key partitions of a causal chunk (SPLIT): partition p holds the 64-key blocks
+// [p * part_blocks, (p + 1) * part_blocks). The boundary part_blocks * 64 = row0 is a
+// multiple of 64, so a 32-token tile lies wholly below it (its rows see one partition and
+// it writes its outputs) or wholly at or above it (every row sees at least two partitions:
+// the tile writes partial states for rows row0.., which the merge kernel combines).
+struct ChunkSplit {
+  float* ws_o;  // [row - row0][head][partition][256] unnormalised outputs
+  float* ws_m;  // running max (exp2 domain)
+  float* ws_l;  // sum of the weights
+  int part_blocks, n_parts, row0;
+};
+
+template <int SPLIT>
 __global__ __launch_bounds__(kCbThreads, 1) void chunk_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int n, int causal, int n_q_heads, int n_kv_heads,
-    float qk_scale_log2, float* __restrict__ out, int n_qb, int xcd_per_head) {
-  int qb, g;
-  {  // XCD-aware order as in the int8 chunk kernel: each KV head on its own XCDs
+    float qk_scale_log2, float* __restrict__ out, int n_qb, int xcd_per_head, ChunkSplit sp) {
+  int qb, g, part = 0;
+  if (SPLIT) {
+    // grid x = (query tile, KV head), the tiles with the most keys first and the heads
+    // interleaved; grid y = the partition (partitions past a tile's keys exit at once).
+    const int x = blockIdx.x;
+    g = x % n_kv_heads;
+    qb = n_qb - 1 - x / n_kv_heads;
+    part = blockIdx.y;
+  } else {  // XCD-aware order as in the int8 chunk kernel: each KV head on its own XCDs
     const int L = blockIdx.x, xcd = L % 8, slot = L / 8;
     if (xcd_per_head > 0) {
       g = xcd / xcd_per_head;
@@ -207,7 +229,11 @@ __global__ __launch_bounds__(kCbThreads, 1) void chunk_bf16_kernel(
   const int my_tok = t0 + 16 * half + nn;
   const int last_tok = min(t0 + kCbTok, n) - 1;
   const int kend = causal ? last_tok + 1 : n;
-  const int nkb = (kend + 63) >> 6;
+  // 64-key blocks [kb0, nkb) of this workgroup
+  const int nkb_tile = (kend + 63) >> 6;
+  const int kb0 = SPLIT ? part * sp.part_blocks : 0;
+  const int nkb = SPLIT ? min(nkb_tile, kb0 + sp.part_blocks) : nkb_tile;
+  if (SPLIT && kb0 >= nkb) return;  // the tile's keys end before this partition
 
   __shared__ __align__(16) int8_t s_k0[kKBytes];
   __shared__ __align__(16) int8_t s_k1[kKBytes];
@@ -216,8 +242,8 @@ __global__ __launch_bounds__(kCbThreads, 1) void chunk_bf16_kernel(
 
   const Loader ld{k, v, n, n_kv_heads, g, w, lane};
   {
-    ld.issue_k(0, s_k0);
-    ld.issue_v(0, s_v0);
+    ld.issue_k(kb0, s_k0);
+    ld.issue_v(kb0, s_v0);
     // Query operands: lane (nn, gq) holds dims 32u + 8gq..+7 of its row (rows past the
     // chunk re-read the last one; their outputs are not stored).
     v8bf qop[8];
@@ -245,7 +271,7 @@ __global__ __launch_bounds__(kCbThreads, 1) void chunk_bf16_kernel(
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) st.acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
     const Block b0{s_k0, s_v0}, b1{s_k1, s_v1};
-    for (int kb = 0; kb < nkb; kb += 2) {
+    for (int kb = kb0; kb < nkb; kb += 2) {
       block_step(kb, nkb, ld, qop, my_tok, t0, causal != 0, n, qk_scale_log2, gq, nn, vaddr, st,
                  b0, b1);
       if (kb + 1 < nkb)
@@ -253,7 +279,20 @@ __global__ __launch_bounds__(kCbThreads, 1) void chunk_bf16_kernel(
                    st, b1, b0);
     }
     const float l = col_sum(st.l_part);
-    if (my_tok < n) {
+    if (SPLIT && nkb_tile > sp.part_blocks) {  // a tile at or above row0: partial state
+      if (my_tok < n) {
+        const size_t pi = ((size_t)(my_tok - sp.row0) * n_q_heads + h) * sp.n_parts + part;
+        float* o = sp.ws_o + pi * kHeadDim + 4 * gq;
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt)
+          *reinterpret_cast<float4*>(o + 16 * dt) =
+              make_float4(st.acc[dt][0], st.acc[dt][1], st.acc[dt][2], st.acc[dt][3]);
+        if (gq == 0) {
+          sp.ws_m[pi] = st.m_run;
+          sp.ws_l[pi] = l;
+        }
+      }
+    } else if (my_tok < n) {
       const float il = 1.0f / l;
       float* o = out + ((size_t)my_tok * n_q_heads + h) * kHeadDim + 4 * gq;
 #pragma unroll
@@ -266,16 +305,59 @@ __global__ __launch_bounds__(kCbThreads, 1) void chunk_bf16_kernel(
 
 }  // namespace
 
+// Partitions for a causal chunk: part_blocks = the 64-key blocks of all (tile, KV head)
+// pairs spread over the 256 CUs (at least 4), so that no workgroup does much more than
+// the average; 1 (the one pass) when no tile reaches past one partition.
+int chunk_bf16_split_parts(int n, int causal, int n_kv_heads, int* part_blocks) {
+  const long long n_qb = (n + kCbTok - 1) / kCbTok;
+  const int nkb_max = (int)(((long long)n + 63) / 64);
+  *part_blocks = nkb_max;
+  if (!causal || n <= 0) return 1;
+  long long total = 0;  // sum over tiles of their 64-key blocks, per KV head
+  for (long long t = 0; t < n_qb; ++t) total += (std::min<long long>(t * kCbTok + kCbTok, n) + 63) / 64;
+  const long long per_cu = (total * n_kv_heads + 255) / 256;
+  const int pb = (int)std::max<long long>(4, per_cu);
+  if (pb >= nkb_max) return 1;
+  *part_blocks = pb;
+  return (nkb_max + pb - 1) / pb;
+}
+
+size_t chunk_bf16_ws_bytes(int n, int causal, int n_q_heads, int n_kv_heads) {
+  int pb;
+  const int parts = chunk_bf16_split_parts(n, causal, n_kv_heads, &pb);
+  if (parts <= 1) return 0;
+  const size_t np = (size_t)(n - pb * 64) * n_q_heads * parts;
+  return ((np * kHeadDim + 2 * np) * sizeof(float) + 255) / 256 * 256;
+}
+
 int launch_chunk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n, int causal,
-                      int n_q_heads, int n_kv_heads, float sm_scale, float* out,
+                      int n_q_heads, int n_kv_heads, float sm_scale, float* out, float* ws,
                       hipStream_t stream) {
   const int n_qb = (n + kCbTok - 1) / kCbTok;
+  ChunkSplit sp{nullptr, nullptr, nullptr, 0, 1, 0};
+  const int n_parts = ws != nullptr ? chunk_bf16_split_parts(n, causal, n_kv_heads, &sp.part_blocks) : 1;
+  if (n_parts > 1) {
+    sp.n_parts = n_parts;
+    sp.row0 = sp.part_blocks * 64;
+    const size_t np = (size_t)(n - sp.row0) * n_q_heads * n_parts;
+    sp.ws_o = ws;
+    sp.ws_m = ws + np * kHeadDim;
+    sp.ws_l = sp.ws_m + np;
+    hipLaunchKernelGGL(chunk_bf16_kernel<1>, dim3((unsigned)(n_qb * n_kv_heads), (unsigned)n_parts),
+                       dim3(kCbThreads), 0, stream, q, k, v, n, causal, n_q_heads, n_kv_heads,
+                       sm_scale * kLog2e, out, n_qb, 0, sp);
+    int rc = check_launch("attn_chunk_bf16");
+    if (rc) return rc;
+    // rows row0.. : n - row0 rows at the tail of an n-key sequence (row t sees t + 1 keys)
+    return launch_merge_rows(sp.ws_m, sp.ws_l, sp.ws_o, n, n - sp.row0, n_q_heads, n_parts,
+                             sp.row0, out + (size_t)sp.row0 * n_q_heads * kHeadDim, stream);
+  }
   const int xcd_per_head = (n_kv_heads <= 8 && 8 % n_kv_heads == 0) ? 8 / n_kv_heads : 0;
   const long long n_wg = xcd_per_head > 0 ? 8LL * ((n_qb + xcd_per_head - 1) / xcd_per_head)
                                           : (long long)n_qb * n_kv_heads;
-  hipLaunchKernelGGL(chunk_bf16_kernel, dim3((unsigned)n_wg), dim3(kCbThreads), 0, stream, q, k,
+  hipLaunchKernelGGL(chunk_bf16_kernel<0>, dim3((unsigned)n_wg), dim3(kCbThreads), 0, stream, q, k,
                      v, n, causal, n_q_heads, n_kv_heads, sm_scale * kLog2e, out, n_qb,
-                     xcd_per_head);
+                     xcd_per_head, sp);
   return check_launch("attn_chunk_bf16");
 }
 

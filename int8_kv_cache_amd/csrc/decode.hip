@@ -427,4 +427,53 @@ int launch_merge(const float* ws_m, const float* ws_l, const float* ws_o, const 
   return check_launch("decode merge");
 }
 
+// Merge for many query rows with few partitions each (the chunk routes' key partitions):
+// one wave per (row, query head), lane l owning dims 4l..4l+3, so each partition's
+// output row is one coalesced 1 KB load; the workgroup holds 4 such pairs. Same
+// combination as decode_merge_kernel: M = max m_j, out = sum_j 2^(m_j - M) o_j /
+// sum_j 2^(m_j - M) l_j over the partitions j that hold a key of the row.
+__global__ __launch_bounds__(256) void merge_rows_kernel(
+    const float* __restrict__ ws_m, const float* __restrict__ ws_l, const float* __restrict__ ws_o,
+    int ctx, int n_q_heads, int n_parts, int nq, int part_rows, float* __restrict__ out,
+    long long n_pairs) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long long pair = (long long)blockIdx.x * 4 + w;
+  if (pair >= n_pairs) return;  // whole wave
+  const int qi = (int)(pair / n_q_heads);
+  const int keys = max(0, ctx - nq + qi + 1);  // keys this query row sees
+  const int P = min(n_parts, (keys + part_rows - 1) / part_rows);
+  const size_t base = (size_t)pair * n_parts;
+  float4* o = reinterpret_cast<float4*>(out + (size_t)pair * kHeadDim) + lane;
+  if (P == 0) {
+    *o = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  float M = -INFINITY;
+  for (int j = 0; j < P; ++j) M = fmaxf(M, ws_m[base + j]);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4* src = reinterpret_cast<const float4*>(ws_o + base * kHeadDim) + lane;
+#pragma unroll 4
+  for (int j = 0; j < P; ++j) {
+    const float a = __builtin_amdgcn_exp2f(ws_m[base + j] - M);
+    const float4 v = src[(size_t)j * (kHeadDim / 4)];
+    L = fmaf(a, ws_l[base + j], L);
+    acc.x = fmaf(a, v.x, acc.x);
+    acc.y = fmaf(a, v.y, acc.y);
+    acc.z = fmaf(a, v.z, acc.z);
+    acc.w = fmaf(a, v.w, acc.w);
+  }
+  const float il = 1.0f / L;
+  *o = make_float4(acc.x * il, acc.y * il, acc.z * il, acc.w * il);
+}
+
+int launch_merge_rows(const float* ws_m, const float* ws_l, const float* ws_o, int ctx, int nq,
+                      int n_q_heads, int n_parts, int part_rows, float* out, hipStream_t stream) {
+  const long long n_pairs = (long long)nq * n_q_heads;
+  hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)((n_pairs + 3) / 4)), dim3(256), 0, stream,
+                     ws_m, ws_l, ws_o, ctx, n_q_heads, n_parts, nq, part_rows, out, n_pairs);
+  return check_launch("merge rows");
+}
+
 }  // namespace i8a

@@ -20,9 +20,13 @@ int launch_kv_produce(const void* q, const void* k, const void* v, int in_bf16, 
                       int8_t* v_cache, float* k_scale, float* v_scale, int num_pages,
                       int8_t* q_codes, float* q_scales, uint16_t* q_rot, uint16_t* k_rot,
                       hipStream_t stream);
+// ws == nullptr: the one pass; otherwise causal chunks whose tiles reach past one key
+// partition run split (chunk_bf16_ws_bytes of scratch) and merged.
 int launch_chunk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n, int causal,
-                      int n_q_heads, int n_kv_heads, float sm_scale, float* out,
+                      int n_q_heads, int n_kv_heads, float sm_scale, float* out, float* ws,
                       hipStream_t stream);
+int chunk_bf16_split_parts(int n, int causal, int n_kv_heads, int* part_blocks);
+size_t chunk_bf16_ws_bytes(int n, int causal, int n_q_heads, int n_kv_heads);
 int launch_q_quant(const uint16_t* q, int n_rows, int8_t* codes, float* scales,
                    hipStream_t stream);
 // q: bf16 rows to quantize (q_scales == nullptr) or int8 codes with q_scales (kv_produce).
@@ -40,6 +44,10 @@ int launch_verify(const void* q, const float* q_scales, int nq, const int8_t* k_
 int launch_merge(const float* ws_m, const float* ws_l, const float* ws_o, const int32_t* ctx_lens,
                  int ctx_cap, int num_seqs, int nq, int n_q_heads, int max_parts, int part_rows,
                  float* out, hipStream_t stream);
+// One sequence's nq query rows at the tail of ctx keys, each with the partial states of
+// up to n_parts key partitions of part_rows keys: [row][head][partition] (m, l, o[256]).
+int launch_merge_rows(const float* ws_m, const float* ws_l, const float* ws_o, int ctx, int nq,
+                      int n_q_heads, int n_parts, int part_rows, float* out, hipStream_t stream);
 int launch_decode_i8pv(int digits, int part_rows, const void* q, const float* q_scales, int nq,
                        const int8_t* k_cache,
                        const int8_t* v_cache, const float* k_scale, const float* v_scale,

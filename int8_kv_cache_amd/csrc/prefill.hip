@@ -497,8 +497,8 @@ int launch_prefill(const void* q, const float* q_scales, int n_new, const int8_t
   int rc = check_launch("attn_prefill_chunk");
   if (rc || n_parts == 1) return rc;
   // Query row t of the chunk sees ctx - n_new + t + 1 keys: the merge of nq = n_new rows.
-  return launch_merge(sp.ws_m, sp.ws_l, sp.ws_o, nullptr, ctx, 1, n_new, n_q_heads, n_parts,
-                      sp.part_blocks * 64, out, stream);
+  return launch_merge_rows(sp.ws_m, sp.ws_l, sp.ws_o, ctx, n_new, n_q_heads, n_parts,
+                           sp.part_blocks * 64, out, stream);
 }
 
 // Partitions for a chunk whose single pass would leave most CUs idle: causal chunks with

@@ -45,6 +45,31 @@ def test_chunk_bf16_matches_exact(n, causal):
     assert err <= TOL * vmax
 
 
+@pytest.mark.parametrize("n,n_kv", [(300, 4), (1000, 1), (700, 3), (2048, 4)])
+def test_chunk_bf16_split_equals_one_pass(n, n_kv):
+    # causal chunks cut into key partitions (workspace given) against the one pass: the
+    # same products and softmax, only the merge's rounding differs; the rows below the
+    # first partition boundary are written by the same code path as the one pass
+    need_gpu()
+    ws = lib.attn_chunk_bf16_workspace_bytes(n, True, 6 * n_kv, n_kv)
+    say(f"attn_chunk_bf16 n={n} with {n_kv} KV heads: split workspace {ws} B vs the one pass")
+    assert ws > 0
+    rng = np.random.default_rng(260 + n)
+    q = rng.standard_normal((n, 6 * n_kv, 256), dtype=np.float32)
+    k = rng.standard_normal((n, n_kv, 256), dtype=np.float32)
+    v = rng.standard_normal((n, n_kv, 256), dtype=np.float32)
+    qb, kb, vb = (_bf16(workloads.f32_to_bf16_bits(a)) for a in (q, k, v))
+    wbuf = torch.full((ws,), 0xff, dtype=torch.uint8, device="cuda")  # NaN bit patterns
+    a = lib.attn_chunk_bf16(qb, kb, vb, causal=True, workspace=wbuf).cpu().numpy()
+    b = lib.attn_chunk_bf16(qb, kb, vb, causal=True, split=False).cpu().numpy()
+    vmax = float(np.max(np.abs(v)))
+    d = float(np.max(np.abs(a - b)))
+    say(f"  max |split - one pass| {d:.3e} (bound {1e-5 * vmax:.3e})")
+    assert np.all(np.isfinite(a)) and d <= 1e-5 * vmax
+    # the first rows of every tile below the boundary are bit-identical
+    assert np.array_equal(a[:64], b[:64])
+
+
 @pytest.mark.parametrize("n_kv", [1, 3])
 def test_chunk_bf16_other_kv_head_counts(n_kv):
     need_gpu()

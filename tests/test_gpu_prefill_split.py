@@ -46,7 +46,7 @@ def _check(st, rows, out):
     (5, 5, 4),         # ... with a single key partition (no merge)
     (3000, 40, 4),     # two query blocks, ragged second
     (3000, 100, 4),    # four query blocks: rows end in different partitions
-    (20000, 12, 1),    # one KV head: more than 64 partitions (the merge's chunk loop)
+    (20000, 12, 1),    # one KV head: 157 partitions per row
     (1000, 500, 4),    # early query blocks stop before the last partition; rows without
                        # a key in a partition keep an empty state there
     (2000, 70, 3),     # three KV heads

@@ -196,10 +196,21 @@ def test_kv_produce_and_q8_validation():
     assert call(3, 7) == C["I8A_EINVAL"]                # dtype
     assert call(4, 0) == C["I8A_OK"]                    # no tokens
     assert call(0, None) == C["I8A_EINVAL"]             # q_codes without q
-    cb = [FAKE, FAKE, FAKE, 64, 2, 24, 4, 256, 0.0625, FAKE, None]
+    cb = [FAKE, FAKE, FAKE, 64, 2, 24, 4, 256, 0.0625, FAKE, None, 0, None]
     assert L.attn_chunk_bf16(*cb) == C["I8A_EINVAL"]    # causal flag
+    # bf16 chunk split: 2,048 causal rows = 1,056 key blocks per KV head over 64 tiles;
+    # x 4 heads / 256 CUs -> 17 blocks per partition, 2 partitions, rows 1,088.. merged
+    cws = m.attn_chunk_bf16_workspace_bytes
+    assert cws(2048, True, 24, 4) == (2048 - 1088) * 24 * 2 * 258 * 4
+    assert cws(2048, False, 24, 4) == 0                 # non-causal: one pass
+    assert cws(64, True, 24, 4) == 0                    # one key block
+    need = cws(2048, True, 24, 4)
+    cb = [FAKE, FAKE, FAKE, 2048, 1, 24, 4, 256, 0.0625, FAKE, FAKE, need - 1, None]
+    assert L.attn_chunk_bf16(*cb) == C["I8A_EWORKSPACE"]
+    cb[10], cb[11] = FAKE + 4, need
+    assert L.attn_chunk_bf16(*cb) == C["I8A_EINVAL"]    # workspace not 16-byte aligned
     ps = m.prefill_step_workspace_bytes(100, 100, 24, 4)   # no history: rotated bf16 Q, K
-    assert ps == (100 * 28 * 256 * 2 + 255) // 256 * 256
+    assert ps == (100 * 28 * 256 * 2 + 255) // 256 * 256 + m.attn_chunk_bf16_workspace_bytes(100, True, 24, 4)
     q8 = (100 * 24 * 260 + 255) // 256 * 256               # history: Q codes + split scratch
     assert m.prefill_step_workspace_bytes(100, 5000, 24, 4) == \
         q8 + m.attn_prefill_chunk_split_workspace_bytes(100, 5000, True, 24, 4)
