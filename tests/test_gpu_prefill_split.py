@@ -79,6 +79,22 @@ def test_split_long_context_sampled():
     _check(st, np.array([0, 1, 15, 16, 31, 32, 47, 62, 63]), out)
 
 
+def test_long_context_both_routes_sampled():
+    # the longest context of the decode workloads (131,072 keys): a 256-row chunk on the
+    # split route (8 query blocks x 4 heads -> 8 partitions of 256 blocks) and on the one
+    # pass, sampled rows against the oracle
+    need_gpu()
+    ctx, n_new = 131072, 256
+    say(f"attn_prefill_chunk(_split) ctx={ctx} n_new={n_new}")
+    st = PrefillSetup(workloads.make_prefill_case(17, ctx, n_new, k_outliers=4))
+    rows = np.array([0, 31, 32, 100, 200, 255])
+    split = _split(st)
+    _check(st, rows, split)
+    one = st.run()
+    _check(st, rows, one)
+    assert np.max(np.abs(split - one)) <= TOL_B * st.vmax
+
+
 @pytest.mark.parametrize("ctx,n_new,causal", [
     (1500, 200, False),   # non-causal: always the one pass
     (5000, 1100, True),   # 35 query blocks x 4 KV heads = 140 workgroups: the one pass
