@@ -410,6 +410,14 @@ def main():
         for _ in range(R):
             lib.attn_decode(q_dec, base, table, ctx_t, ctx, out=out_dec, workspace=ws)
     warm_us = per_call_us(warm8, R)
+    # kv_quant_write of a whole 32,768-token context in one call (fp32 rows in): the
+    # HBM-bound regime of the writer, against the 2,048-row call of the step
+    k_all, v_all, s_all = up(k4), up(v4), up(slots4)
+    qw_big_us = per_call_us(lambda: lib.kv_quant_write(k_all, v_all, s_all, pcache), 1, reps=10)
+    qw_big_b = quant_write_bytes(pf.context_len, pf.n_kv_heads, pf.head_dim)
+    res["quant_write_32768"] = {"us": round(qw_big_us, 2), "bytes": qw_big_b,
+                                "hbm_GBps": round(qw_big_b / (qw_big_us * 1e-6) / 1e9, 1)}
+    del k_all, v_all, s_all
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
