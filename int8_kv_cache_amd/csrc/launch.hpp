@@ -41,6 +41,7 @@ int launch_verify(const void* q, const float* q_scales, int nq, const int8_t* k_
                   int max_blocks, const int32_t* ctx_lens, int num_seqs, int max_ctx,
                   int num_pages, int n_q_heads, int n_kv_heads, float sm_scale, float* out,
                   float* ws, int max_parts, hipStream_t stream);
+// ctx_lens == nullptr (here and in launch_decode_i8pv): one sequence of ctx_cap keys.
 int launch_merge(const float* ws_m, const float* ws_l, const float* ws_o, const int32_t* ctx_lens,
                  int ctx_cap, int num_seqs, int nq, int n_q_heads, int max_parts, int part_rows,
                  float* out, hipStream_t stream);
