@@ -430,6 +430,70 @@ def main():
         for c in copies:
             lib.attn_decode(q_dec, c, table, ctx_t, ctx, out=out_dec, workspace=ws)
     graph_us = per_call_us(dgraph.replay, R)
+    # the other decode workloads: configs 1 and 2 (one sequence, ctx 256 and 3,328; eager
+    # calls and 16 calls replayed from a graph) and config 5 (64 sequences, contexts
+    # log-uniform in [1,024, 131,072], 3.6 GB of K/V: MALL-cold by size). Config 5's K/V
+    # rows are drawn on the GPU (N(0,1)) into the config's page tables: the decode time
+    # does not depend on the values.
+    def decode_graph_us(call, n_calls=16):
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            call()
+        torch.cuda.current_stream().wait_stream(s2)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n_calls):
+                call()
+        return per_call_us(g.replay, n_calls)
+
+    dcfg = {}
+    for cfg in (1, 2):
+        c = workloads.config_case(cfg)
+        kk, vv, qq, ss = c.all_data()
+        cc = lib.alloc_cache(c.num_pages, c.n_kv_heads, dev)
+        lib.kv_quant_write(up(kk), up(vv), up(ss), cc)
+        qd, tb, cl = bf16(qq[:, 0]), up(c.block_table), up(c.context_lens)
+        od = torch.empty((c.num_seqs, c.n_q_heads, c.head_dim), dtype=torch.float32, device=dev)
+        wd = torch.empty(max(lib.attn_decode_workspace_bytes(c.num_seqs, c.max_context_len,
+                                                             c.n_q_heads), 256),
+                         dtype=torch.uint8, device=dev)
+
+        def call(qd=qd, cc=cc, tb=tb, cl=cl, c=c, od=od, wd=wd):
+            lib.attn_decode(qd, cc, tb, cl, c.max_context_len, out=od, workspace=wd)
+        eager = per_call_us(lambda: [call() for _ in range(16)], 16)
+        graph = decode_graph_us(call)
+        nbytes = decode_bytes(c.max_context_len, c.n_q_heads, c.n_kv_heads, c.head_dim)
+        dcfg[f"config{cfg}"] = {"ctx": c.max_context_len, "bytes": nbytes,
+                                "us_eager": round(eager, 3), "us_graph": round(graph, 3),
+                                "GBps_graph": round(nbytes / (graph * 1e-6) / 1e9, 1)}
+    c5 = workloads.config_case(5)
+    cache5 = lib.alloc_cache(c5.num_pages, c5.n_kv_heads, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(c5.seed)
+    for s_ in range(c5.num_seqs):
+        sl5 = up(c5.seq_slots(s_))
+        for t0 in range(0, int(c5.context_lens[s_]), 65536):
+            nrow = min(65536, int(c5.context_lens[s_]) - t0)
+            shp = (nrow, c5.n_kv_heads, c5.head_dim)
+            lib.kv_quant_write(torch.randn(shp, generator=gen, device=dev),
+                               torch.randn(shp, generator=gen, device=dev), sl5[t0:t0 + nrow],
+                               cache5)
+    q5 = torch.randn((c5.num_seqs, c5.n_q_heads, c5.head_dim), generator=gen,
+                     device=dev).to(torch.bfloat16)
+    tb5, cl5 = up(c5.block_table), up(c5.context_lens)
+    o5 = torch.empty((c5.num_seqs, c5.n_q_heads, c5.head_dim), dtype=torch.float32, device=dev)
+    w5 = torch.empty(lib.attn_decode_workspace_bytes(c5.num_seqs, c5.max_context_len,
+                                                     c5.n_q_heads), dtype=torch.uint8, device=dev)
+    t5 = per_call_us(lambda: lib.attn_decode(q5, cache5, tb5, cl5, c5.max_context_len, out=o5,
+                                             workspace=w5), 1, reps=10)
+    b5 = sum(decode_bytes(int(x), c5.n_q_heads, c5.n_kv_heads, c5.head_dim) for x in c5.context_lens)
+    dcfg["config5"] = {"seqs": c5.num_seqs, "total_ctx": c5.total_tokens, "bytes": b5,
+                       "us": round(t5, 2), "hbm_GBps": round(b5 / (t5 * 1e-6) / 1e9, 1),
+                       "frac_of_8TBps": round(b5 / (t5 * 1e-6) / 8e12, 4)}
+    del cache5, w5
+    res["decode_configs"] = dcfg
     res["decode_us_mall_warm"] = round(warm_us, 3)
     res["decode_us_graph"] = round(graph_us, 3)
     nb = 1 << 30
