@@ -27,7 +27,8 @@ namespace i8a {
 
 constexpr int kPart = 512;
 constexpr int kDecWaves = 8;
-constexpr int kFlatMaxSeqs = 4096;     // batches up to this size take the flattened grid
+constexpr int kFlatMinSeqs = 16;       // batches of this size and up to kFlatMaxSeqs take
+constexpr int kFlatMaxSeqs = 4096;     // the flattened grid
 constexpr int kFlatWorkgroups = 256;  // one per CU (the split kernel fits one per CU)
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
@@ -206,9 +207,12 @@ int launch_decode(const void* q, const float* q_scales, const int8_t* k_cache, c
   float* ws_o = ws + 2 * np;
   const long long cap = (long long)max_blocks * kPage;
   const int ctx_cap = (int)(cap < max_ctx ? cap : max_ctx);
-  // One sequence (or a batch past kFlatMaxSeqs): the (partition, head, sequence) grid.
-  // A batch: the flattened grid of real work items, one workgroup per CU at most.
-  const bool flat = num_seqs > 1 && num_seqs <= kFlatMaxSeqs;
+  // Batches of kFlatMinSeqs..kFlatMaxSeqs sequences: the flattened grid of real work
+  // items, one workgroup per CU; otherwise the (partition, head, sequence) grid. (The
+  // flattened loop costs ~1 us more per item than a fresh workgroup, so it wins where
+  // the grid would hold many partitions past their sequence's end -- unequal lengths --
+  // and loses a few percent on batches of equal lengths; small batches keep the grid.)
+  const bool flat = num_seqs >= kFlatMinSeqs && num_seqs <= kFlatMaxSeqs;
   const long long items_max = (long long)num_seqs * max_parts * n_kv_heads;
   const dim3 grid = flat ? dim3((unsigned)(items_max < kFlatWorkgroups ? items_max : kFlatWorkgroups))
                          : dim3(max_parts, n_kv_heads, num_seqs);

@@ -35,11 +35,48 @@ def test_decode_configs(cfg):
     _check_all(DecodeSetup(workloads.config_case(cfg)))
 
 
-def test_decode_edge_contexts_batched():
+EDGE_CTX = [1, 2, 15, 16, 17, 63, 64, 65, 100, 511, 512, 513, 1023, 1024, 1300, 2049]
+
+
+@pytest.mark.parametrize("n_seqs", [15, 16, 40])
+def test_decode_edge_contexts_batched(n_seqs):
+    # 15 sequences: the (partition, head, sequence) grid; 16 and more: the flattened grid
+    # of real work items
     need_gpu()
-    ctx = [1, 2, 15, 16, 17, 63, 64, 65, 100, 511, 512, 513, 1023, 1024, 1300, 2049]
-    say(f"attn_decode edge contexts {ctx}")
+    ctx = (EDGE_CTX * 3)[:n_seqs]
+    say(f"attn_decode edge contexts, {n_seqs} sequences: {ctx}")
     case = workloads.make_decode_case(41, ctx, pages="random", k_outliers=4, extra_pages=5)
+    _check_all(DecodeSetup(case))
+
+
+@pytest.mark.parametrize("n_seqs", [3, 20])
+def test_decode_zero_contexts_give_zeros(n_seqs):
+    # a context length of 0 (or below 0) in the batch gives zeros for that sequence and
+    # leaves the others exact, on both grids; all contexts <= 512 (no merge stage) and
+    # longer ones
+    need_gpu()
+    rng = np.random.default_rng(n_seqs)
+    for hi in (512, 3000):
+        ctx = list(rng.integers(1, hi + 1, n_seqs))
+        say(f"attn_decode {n_seqs} sequences, contexts up to {hi}, two set to 0 and -5")
+        st = DecodeSetup(workloads.make_decode_case(48 + hi, ctx, pages="random", k_outliers=4))
+        zero = [0, n_seqs - 1]
+        c = st.case.context_lens.copy()
+        c[zero[0]], c[zero[1]] = 0, -5
+        st.ctx = up(c)
+        out = st.run()
+        for s in zero:
+            assert np.all(out[s] == 0.0)
+        for s in range(1, n_seqs - 1):
+            assert np.max(np.abs(out[s] - st.oracle_out(s))) <= TOL * st.vmax
+
+
+def test_decode_flat_grid_one_kv_head():
+    need_gpu()
+    ctx = [700, 1, 5000, 513, 64, 2100, 90, 1024] * 3
+    say(f"attn_decode {len(ctx)} sequences with 1 KV head x 6 query heads")
+    case = workloads.make_decode_case(85, ctx, pages="random", k_outliers=4, n_q_heads=6,
+                                      n_kv_heads=1)
     _check_all(DecodeSetup(case))
 
 
