@@ -68,6 +68,22 @@ def test_int8p_verify_rows(nq):
     _check(st, st.run_int8p(partition_rows=64))
 
 
+def test_int8p_batch_flattened_grid():
+    # 20 sequences with 512-key partitions: the flattened grid of real work items; the
+    # same batch at 64-key partitions keeps the grid (both to the oracle), and rows before
+    # their context (context 2 with 4 rows) are 0
+    need_gpu()
+    nq = 4
+    ctx = [2, 70, 512 + nq - 2, 1030, 3000] * 4
+    case = workloads.make_decode_case(97, ctx, pages="random", k_outliers=4, q_rows_per_seq=nq)
+    say(f"attn_decode_int8p nq={nq}, {len(ctx)} sequences")
+    st = DecodeSetup(case)
+    out = st.run_int8p(partition_rows=512)
+    assert np.all(out[0, :2] == 0.0)
+    _check(st, out)
+    _check(st, st.run_int8p(partition_rows=64))
+
+
 def test_int8p_rows_before_the_context_are_zero():
     need_gpu()
     case = workloads.make_decode_case(95, [2, 3], pages="random", q_rows_per_seq=4)

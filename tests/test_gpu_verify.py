@@ -39,6 +39,18 @@ def test_verify_ragged_contexts(nq):
     _check(st, st.run_verify())
 
 
+@pytest.mark.parametrize("nq", [2, 4])
+def test_verify_batch_flattened_grid(nq):
+    # 24 sequences: the flattened grid of real work items (batches of 16 and more)
+    need_gpu()
+    ctx = [nq, 17, 64 + nq - 1, 300, 512 + nq - 2, 513, 1024 + 3, 2049] * 3
+    say(f"attn_verify nq={nq}, {len(ctx)} sequences")
+    case = workloads.make_decode_case(90 + nq, ctx, pages="random", k_outliers=4, extra_pages=3,
+                                      q_rows_per_seq=nq)
+    st = DecodeSetup(case)
+    _check(st, st.run_verify())
+
+
 def test_verify_one_row_is_decode():
     need_gpu()
     case = workloads.make_decode_case(80, [1, 700, 1537], pages="random", k_outliers=4)
