@@ -23,7 +23,8 @@
 //    reference max only moves when a block max exceeds it by more than 2^8, so
 //    p <= 256);
 //  * w = p * sV, per (row, block) s_b = max w / 127, codes rint(w / s_b) in [0, 127]
-//    (v_cvt_pk_u8_f32 converts and packs); the denominator sums the unquantized p;
+//    (one fma onto 1.5 * 2^23 rounds each to an integer in the low mantissa bits, two
+//    byte permutes pack four); the denominator sums the unquantized p;
 //  * out^T += s_b * (V^T . P^T) on v_mfma_i32_16x16x64_i8, exact in int32 per block.
 //    The product is accumulated onto the bit pattern of 1.5 * 2^23 (|V^T . P^T| <=
 //    64 * 127 * 127 < 2^22), so read as fp32 it is 1.5 * 2^23 + the exact integer and
@@ -217,15 +218,19 @@ __device__ __forceinline__ void block_step(
   wm = col_max(wm);
   // 127 / wm via the hardware reciprocal (about 1 ulp): a code can move only at an
   // exact rounding tie, and w * inv stays below 127.5, so codes never exceed 127.
+  // fma(w, inv, 1.5 * 2^23) lies in [2^23, 2^24), where the fp32 spacing is 1, so its
+  // single rounding (to nearest even) leaves rint(w * inv) in the low byte.
   const float inv = wm > 0.f ? 127.0f * __builtin_amdgcn_rcpf(wm) : 0.f;
   const float sb = wm * (1.0f / 127.0f);
   v4i Pb;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    uint32_t d = 0u;
+    uint32_t r[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * t + i] * inv, i, d);
-    Pb[t] = (int)d;
+    for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(fmaf(y[4 * t + i], inv, kMagicF));
+    const uint32_t lo = __builtin_amdgcn_perm(r[1], r[0], 0x0c0c0400u);  // [r0.b0, r1.b0, 0, 0]
+    const uint32_t hi = __builtin_amdgcn_perm(r[3], r[2], 0x04000c0cu);  // [0, 0, r2.b0, r3.b0]
+    Pb[t] = (int)(lo | hi);
   }
 
   // PV: out^T(dim tile dt) += s_b * V^T(dt) . P^T; the A operand of lane (n, gq) is
