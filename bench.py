@@ -494,6 +494,26 @@ def main():
                        "frac_of_8TBps": round(b5 / (t5 * 1e-6) / 8e12, 4)}
     del cache5, w5
     res["decode_configs"] = dcfg
+    # one chunked-prefill step end to end (producer: RoPE, quantization and paged write of
+    # the new rows; then the int8 chunk on the split route) for the last 64 and 256 rows
+    # of the 32,768-token prefill context; it rewrites those rows' pages, so it runs last
+    steps_e2e = {}
+    for n in (64, 256):
+        sl = slice(pf.n_new - n, pf.n_new)
+        ws_st = torch.empty(lib.prefill_step_workspace_bytes(n, pf.context_len, pf.n_q_heads,
+                                                             pf.n_kv_heads), dtype=torch.uint8,
+                            device=dev)
+        o_st = torch.empty((n, pf.n_q_heads, pf.head_dim), dtype=torch.float32, device=dev)
+        args_st = (qb[sl], kb[sl], vb[sl], pos_t[sl], rope_tab, s_chunk[sl], pcache, ptable,
+                   pf.context_len)
+        t_st = per_call_us(lambda: lib.prefill_step(*args_st, out=o_st, workspace=ws_st), 1,
+                           reps=10)
+        # (eager calls at 64 rows are bound by the Python wrapper's argument checks; the
+        # graph replay shows the GPU time)
+        t_gr = decode_graph_us(lambda: lib.prefill_step(*args_st, out=o_st, workspace=ws_st),
+                               n_calls=4)
+        steps_e2e[f"n{n}"] = {"us_eager": round(t_st, 2), "us_graph": round(t_gr, 2)}
+    res["prefill_step_ctx32768"] = steps_e2e
     res["decode_us_mall_warm"] = round(warm_us, 3)
     res["decode_us_graph"] = round(graph_us, 3)
     nb = 1 << 30
