@@ -84,6 +84,20 @@ def test_int8p_batch_flattened_grid():
     _check(st, st.run_int8p(partition_rows=64))
 
 
+def test_int8p_batch_flattened_grid_single_partition():
+    # 18 sequences, every context within one 512-key partition: the flattened grid writes
+    # the normalized rows itself (no merge stage)
+    need_gpu()
+    nq = 2
+    ctx = [1, 2, 37, 300, 511, 512] * 3
+    case = workloads.make_decode_case(98, ctx, pages="random", k_outliers=4, q_rows_per_seq=nq)
+    say(f"attn_decode_int8p nq={nq}, {len(ctx)} sequences of at most 512 keys")
+    st = DecodeSetup(case)
+    out = st.run_int8p(partition_rows=512)
+    assert np.all(out[0, :1] == 0.0)
+    _check(st, out)
+
+
 def test_int8p_rows_before_the_context_are_zero():
     need_gpu()
     case = workloads.make_decode_case(95, [2, 3], pages="random", q_rows_per_seq=4)

@@ -51,6 +51,17 @@ def test_verify_batch_flattened_grid(nq):
     _check(st, st.run_verify())
 
 
+def test_verify_batch_flattened_grid_single_partition():
+    # 18 sequences of at most 512 keys: the flattened grid without a merge stage
+    need_gpu()
+    nq = 3
+    ctx = [3, 20, 64, 300, 511, 512] * 3
+    say(f"attn_verify nq={nq}, {len(ctx)} sequences of at most 512 keys")
+    case = workloads.make_decode_case(99, ctx, pages="random", k_outliers=4, q_rows_per_seq=nq)
+    st = DecodeSetup(case)
+    _check(st, st.run_verify())
+
+
 def test_verify_one_row_is_decode():
     need_gpu()
     case = workloads.make_decode_case(80, [1, 700, 1537], pages="random", k_outliers=4)
