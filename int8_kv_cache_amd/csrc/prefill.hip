@@ -279,8 +279,8 @@ __device__ __forceinline__ void block_step(
 // bf16 rows to quantize.
 // SPLIT: the keys are cut into partitions of part_blocks 64-key blocks, one workgroup per
 // (KV head, partition, query block); each writes the partial softmax state (max, sum,
-// unnormalised output) of its rows over its partition, and the decode merge kernel
-// combines them.
+// unnormalised output) of its rows over its partition, and the row merge kernel
+// (merge_rows_kernel) combines them.
 struct SplitOut {
   float* ws_m;
   float* ws_l;
