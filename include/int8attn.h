@@ -234,8 +234,11 @@ size_t attn_decode_workspace_bytes(int num_seqs, int max_context_len,
  *                keys produces zeros.
  *  max_context_len   >= every context_lens[s] (sets the launch grid).
  *  num_pages     pool size; a table entry outside [0, num_pages) reads page 0 instead
- *                (memory-safe, result unspecified).
- *  sm_scale      softmax scale, normally 1/sqrt(head_dim) = 1/16 [DCU §1.3].
+ *                (memory-safe, result unspecified; int8attn_check_block_table reports
+ *                such entries).
+ *  sm_scale      softmax scale, normally 1/sqrt(head_dim) = 1/16 [DCU §1.3]; every
+ *                attention entry point refuses a scale that is negative or not finite
+ *                (I8A_EINVAL).
  *  out           fp32 [num_seqs][n_q_heads][head_dim], fully overwritten.
  *  workspace     >= attn_decode_workspace_bytes(...) bytes, device memory, contents
  *                undefined after the call. Calls sharing one workspace must be ordered
@@ -431,6 +434,36 @@ int attn_prefill_chunk_split_q8(const int8_t* q_codes, const float* q_scales, in
                                 int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
                                 float sm_scale, float* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Opt-in validation of the paging metadata (host arrays).
+ * The kernels do not check table entries or slots one by one: an entry outside the
+ * pool reads page 0 (memory-safe, but a wrong page's keys enter the result) and a slot
+ * outside the pool is skipped by the writers. A caller that wants such mistakes to be
+ * errors runs these checks on HOST copies of the arrays before the call (they
+ * synchronize with nothing and touch no device memory). [DCU §5.4: a fast kernel that
+ * reads the wrong fragment gives plausible but wrong attention; checks that tie every
+ * index to the data it names are what catches it.]
+ * Both return I8A_OK, or I8A_EINVAL with int8attn_last_error() naming the first
+ * offending entry. */
+
+/* int8attn_check_block_table -- for every sequence s (context_lens NULL: one context of
+ * max_context_len per sequence, as attn_prefill_chunk's single table row):
+ *  - 0 <= context_lens[s] <= max_context_len and <= 16 * max_blocks_per_seq;
+ *  - each of the ceil(ctx/16) table entries the sequence uses lies in [0, num_pages).
+ * Entries past a sequence's context are not read by the kernels and not checked.
+ *  block_table   int32 [num_seqs][max_blocks_per_seq], host memory.
+ *  context_lens  int32 [num_seqs], host memory, or NULL. */
+int int8attn_check_block_table(const int32_t* block_table, int num_seqs,
+                               int max_blocks_per_seq, const int32_t* context_lens,
+                               int max_context_len, int num_pages);
+
+/* int8attn_check_slots -- slot_mapping int32 [n_tokens] (host memory) as kv_quant_write
+ * and kv_produce take it: a slot >= num_pages * 16 is an error (the writers would skip
+ * the token silently), and so is a slot named by two tokens (the writers leave it
+ * unspecified which one wins). Negative slots are the documented "skip this token" and
+ * pass. */
+int int8attn_check_slots(const int32_t* slot_mapping, int n_tokens, int num_pages);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ __all__ = ["lib", "PagedCache", "alloc_cache", "kv_quant_write", "q_quant", "att
            "attn_prefill_chunk", "attn_prefill_chunk_split",
            "attn_prefill_chunk_split_workspace_bytes", "kv_produce", "attn_chunk_bf16",
            "attn_chunk_bf16_workspace_bytes", "prefill_step",
-           "prefill_step_workspace_bytes", "Int8AttnError",
+           "prefill_step_workspace_bytes", "check_block_table", "check_slots", "Int8AttnError",
            "HEAD_DIM", "PAGE", "PARTITION", "EXPORTED_SYMBOLS"]
 
 HEAD_DIM = 256
@@ -37,7 +37,8 @@ EXPORTED_SYMBOLS = ("int8attn_last_error", "int8attn_version", "kv_quant_write",
                     "attn_decode_int8p_workspace_bytes", "attn_decode_int8p",
                     "attn_prefill_chunk", "attn_prefill_chunk_split_workspace_bytes",
                     "attn_prefill_chunk_split", "attn_prefill_chunk_split_q8",
-                    "attn_chunk_bf16_workspace_bytes")
+                    "attn_chunk_bf16_workspace_bytes", "int8attn_check_block_table",
+                    "int8attn_check_slots")
 
 _c_void = ctypes.c_void_p
 _c_int = ctypes.c_int
@@ -96,6 +97,8 @@ _SIGNATURES = {
     "attn_prefill_chunk_split": (_c_int, [_c_void, _c_int, _c_void, _c_void, _c_void, _c_void,
                                           _c_void, _c_int, _c_int, _c_int, _c_int, _c_int,
                                           _c_int, _c_float, _c_void, _c_void, _c_size, _c_void]),
+    "int8attn_check_block_table": (_c_int, [_c_void, _c_int, _c_int, _c_void, _c_int, _c_int]),
+    "int8attn_check_slots": (_c_int, [_c_void, _c_int, _c_int]),
     "attn_prefill_chunk_split_q8": (_c_int, [_c_void, _c_void, _c_int, _c_void, _c_void,
                                              _c_void, _c_void, _c_void, _c_int, _c_int, _c_int,
                                              _c_int, _c_int, _c_int, _c_float, _c_void, _c_void,
@@ -510,3 +513,39 @@ def attn_prefill_chunk_split(q: torch.Tensor, cache, block_table: torch.Tensor, 
               _dev(out, "out", torch.float32), _dev(workspace, "workspace"),
               workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def _host_i32(a, name: str):
+    """A host int32 contiguous copy of a numpy array or torch tensor (any device)."""
+    import numpy as np
+    if isinstance(a, torch.Tensor):
+        a = a.detach().to("cpu").numpy()
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.int32:
+        raise TypeError(f"{name} must be int32, got {a.dtype}")
+    return a
+
+
+def check_block_table(block_table, context_lens, max_context_len: int, num_pages: int) -> None:
+    """Opt-in check of paging metadata (int8attn_check_block_table on host copies):
+    block_table [S, max_blocks] with context_lens [S], or a single table row [blocks] with
+    context_lens None (one sequence of max_context_len keys, as attn_prefill_chunk takes).
+    Raises Int8AttnError naming the first entry outside the pool or bad context length."""
+    t = _host_i32(block_table, "block_table")
+    if t.ndim == 1:
+        t = t[None, :]
+    if t.ndim != 2:
+        raise ValueError("block_table must be [S, max_blocks] or [blocks]")
+    c = None if context_lens is None else _host_i32(context_lens, "context_lens")
+    if c is not None and c.shape != (t.shape[0],):
+        raise ValueError("context_lens must be [S]")
+    _check(lib().int8attn_check_block_table(t.ctypes.data, t.shape[0], t.shape[1],
+                                            None if c is None else c.ctypes.data,
+                                            int(max_context_len), int(num_pages)))
+
+
+def check_slots(slot_mapping, num_pages: int) -> None:
+    """Opt-in check of a writer's slot_mapping [T] (int8attn_check_slots on a host copy):
+    raises Int8AttnError for a slot outside the pool or one named by two tokens."""
+    s = _host_i32(slot_mapping, "slot_mapping").reshape(-1)
+    _check(lib().int8attn_check_slots(s.ctypes.data, s.shape[0], int(num_pages)))

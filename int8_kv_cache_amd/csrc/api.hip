@@ -1,11 +1,14 @@
 // extern "C" entry points: argument validation, workspace sizing, launch, error codes.
-// Nothing here allocates or synchronizes; every check happens before anything is
-// enqueued, so an error leaves every output untouched.
+// Nothing here allocates device memory or synchronizes; every check happens before
+// anything is enqueued, so an error leaves every output untouched. (The opt-in metadata
+// checks at the end work on host arrays and use host memory only.)
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
+#include <vector>
 
 #include "int8attn.h"
 #include "launch.hpp"
@@ -27,6 +30,14 @@ int set_error(int code, const char* fmt, ...) {
 int check_launch(const char* what) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(I8A_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return I8A_OK;
+}
+
+// The softmax scale must be finite and not negative: the chunk kernel bounds its running
+// max through the scale's sign, so a negative scale is refused on every route alike.
+static int check_sm_scale(const char* who, float sm_scale) {
+  if (!isfinite(sm_scale) || sm_scale < 0.0f)
+    return set_error(I8A_EINVAL, "%s: sm_scale %g (must be finite and >= 0)", who, (double)sm_scale);
   return I8A_OK;
 }
 
@@ -144,7 +155,7 @@ int attn_chunk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
   if (rc) return rc;
   if (n < 0 || (causal != 0 && causal != 1) || (long long)n * n_q_heads > 2147483000LL)
     return set_error(I8A_EINVAL, "attn_chunk_bf16: n %d, causal %d", n, causal);
-  if (!isfinite(sm_scale)) return set_error(I8A_EINVAL, "attn_chunk_bf16: sm_scale not finite");
+  if ((rc = check_sm_scale("attn_chunk_bf16", sm_scale))) return rc;
   size_t need = 0;
   if (workspace != nullptr) {
     if (((uintptr_t)workspace & 15u) != 0)
@@ -192,7 +203,14 @@ int prefill_step(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n_
   if (rc) return rc;
   if (n_new < 0 || context_len < n_new || context_len < 1)
     return set_error(I8A_EINVAL, "prefill_step: n_new %d, context_len %d", n_new, context_len);
+  // (checked before the producer runs, so that a refused call enqueues nothing)
+  if ((rc = check_sm_scale("prefill_step", sm_scale))) return rc;
   if (n_new == 0) return I8A_OK;
+  if (!out || (context_len > n_new && !block_table))
+    return set_error(I8A_EINVAL, "prefill_step: null out or block_table");
+  if ((long long)num_pages * n_kv_heads * 16 >= (1ll << 32))
+    return set_error(I8A_EUNSUPPORTED, "prefill_step: num_pages %d x %d heads exceeds the scale index range",
+                     num_pages, n_kv_heads);
   if (!workspace || ((uintptr_t)workspace & 255u) != 0)
     return set_error(I8A_EINVAL, "prefill_step: workspace null or not 256-byte aligned");
   const size_t need = prefill_step_workspace_bytes(n_new, context_len, n_q_heads, n_kv_heads, head_dim);
@@ -257,7 +275,7 @@ static int decode_impl(const void* q, const float* q_scales, const int8_t* k_cac
   if (max_context_len <= 0 || max_blocks_per_seq <= 0 || num_pages <= 0)
     return set_error(I8A_EINVAL, "attn_decode: max_context_len %d, max_blocks_per_seq %d, num_pages %d",
                      max_context_len, max_blocks_per_seq, num_pages);
-  if (!isfinite(sm_scale)) return set_error(I8A_EINVAL, "attn_decode: sm_scale not finite");
+  if ((rc = check_sm_scale("attn_decode", sm_scale))) return rc;
   if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_table || !context_lens || !out ||
       !workspace)
     return set_error(I8A_EINVAL, "attn_decode: null pointer");
@@ -319,7 +337,7 @@ static int verify_impl(const void* q, const float* q_scales, int nq, const int8_
   if (max_context_len <= 0 || max_blocks_per_seq <= 0 || num_pages <= 0)
     return set_error(I8A_EINVAL, "attn_verify: max_context_len %d, max_blocks_per_seq %d, num_pages %d",
                      max_context_len, max_blocks_per_seq, num_pages);
-  if (!isfinite(sm_scale)) return set_error(I8A_EINVAL, "attn_verify: sm_scale not finite");
+  if ((rc = check_sm_scale("attn_verify", sm_scale))) return rc;
   if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_table || !context_lens || !out ||
       !workspace)
     return set_error(I8A_EINVAL, "attn_verify: null pointer");
@@ -401,7 +419,7 @@ static int int8p_impl(const void* q, const float* q_scales, int nq, const int8_t
   if (part < 0)
     return set_error(I8A_EINVAL, "attn_decode_int8p: partition_rows %d (0, 64, 128, 256 or 512)",
                      partition_rows);
-  if (!isfinite(sm_scale)) return set_error(I8A_EINVAL, "attn_decode_int8p: sm_scale not finite");
+  if ((rc = check_sm_scale("attn_decode_int8p", sm_scale))) return rc;
   if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_table || !context_lens || !out ||
       !workspace)
     return set_error(I8A_EINVAL, "attn_decode_int8p: null pointer");
@@ -485,7 +503,7 @@ static int prefill_impl(const void* q, const float* q_scales, int n_new, const i
   if ((long long)num_pages * n_kv_heads * 16 >= (1ll << 32))
     return set_error(I8A_EUNSUPPORTED, "attn_prefill_chunk: num_pages %d x %d heads exceeds the scale index range",
                      num_pages, n_kv_heads);
-  if (!isfinite(sm_scale)) return set_error(I8A_EINVAL, "attn_prefill_chunk: sm_scale not finite");
+  if ((rc = check_sm_scale("attn_prefill_chunk", sm_scale))) return rc;
   if (n_new == 0) return I8A_OK;
   if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_table || !out)
     return set_error(I8A_EINVAL, "attn_prefill_chunk: null pointer");
@@ -553,6 +571,53 @@ int attn_prefill_chunk_split_q8(const int8_t* q_codes, const float* q_scales, in
   return prefill_impl(q_codes, q_scales, n_new, k_cache, v_cache, k_scale, v_scale, block_table,
                       context_len, causal, num_pages, n_q_heads, n_kv_heads, head_dim, sm_scale,
                       out, 1, workspace, workspace_bytes, stream);
+}
+
+// Opt-in checks of the paging metadata on host copies. The kernels map an entry outside
+// the pool to page 0 (memory-safe, result unspecified) and the writers skip slots outside
+// the pool; these calls turn such entries into an error that names the first offender.
+int int8attn_check_block_table(const int32_t* block_table, int num_seqs, int max_blocks_per_seq,
+                               const int32_t* context_lens, int max_context_len, int num_pages) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_pages <= 0)
+    return set_error(I8A_EINVAL, "check_block_table: num_seqs %d, max_blocks_per_seq %d, "
+                     "max_context_len %d, num_pages %d", num_seqs, max_blocks_per_seq,
+                     max_context_len, num_pages);
+  if (num_seqs > 0 && !block_table) return set_error(I8A_EINVAL, "check_block_table: null table");
+  const long long cap = (long long)max_blocks_per_seq * 16;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int ctx = context_lens ? context_lens[s] : max_context_len;
+    if (ctx < 0 || ctx > max_context_len || ctx > cap)
+      return set_error(I8A_EINVAL, "check_block_table: sequence %d has context %d (0 .. min(%d, "
+                       "16 x %d blocks))", s, ctx, max_context_len, max_blocks_per_seq);
+    const int32_t* row = block_table + (size_t)s * max_blocks_per_seq;
+    for (int b = 0; b < (ctx + 15) / 16; ++b)
+      if (row[b] < 0 || row[b] >= num_pages)
+        return set_error(I8A_EINVAL, "check_block_table: sequence %d block %d (tokens %d..%d) "
+                         "names page %d outside the pool of %d pages", s, b, 16 * b,
+                         ctx < 16 * b + 16 ? ctx - 1 : 16 * b + 15, (int)row[b], num_pages);
+  }
+  return I8A_OK;
+}
+
+int int8attn_check_slots(const int32_t* slot_mapping, int n_tokens, int num_pages) {
+  if (n_tokens < 0 || num_pages <= 0 || (long long)num_pages * 16 > 2147483647LL)
+    return set_error(I8A_EINVAL, "check_slots: n_tokens %d, num_pages %d", n_tokens, num_pages);
+  if (n_tokens > 0 && !slot_mapping) return set_error(I8A_EINVAL, "check_slots: null slot_mapping");
+  const int n_slots = num_pages * 16;
+  std::vector<int32_t> seen;
+  seen.reserve(n_tokens);
+  for (int t = 0; t < n_tokens; ++t) {
+    const int32_t sl = slot_mapping[t];
+    if (sl >= n_slots)
+      return set_error(I8A_EINVAL, "check_slots: token %d has slot %d outside the pool of %d slots",
+                       t, (int)sl, n_slots);
+    if (sl >= 0) seen.push_back(sl);
+  }
+  std::sort(seen.begin(), seen.end());
+  for (size_t i = 1; i < seen.size(); ++i)
+    if (seen[i] == seen[i - 1])
+      return set_error(I8A_EINVAL, "check_slots: slot %d is named by two tokens", (int)seen[i]);
+  return I8A_OK;
 }
 
 }  // extern "C"

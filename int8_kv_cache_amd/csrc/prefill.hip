@@ -73,7 +73,9 @@ struct BlockLoader {
     for (int t = 0; t < 4; ++t) r.p[t] = block_table[min(kb * 4 + t, n_table - 1)];
     return r;
   }
-  // Entries past the context or outside the pool read page 0 (their keys are masked).
+  // Entries past the context read page 0, and their keys are masked. An entry outside
+  // the pool inside the context also reads page 0, whose keys then enter the result: it
+  // is memory-safe but wrong (int8attn_check_block_table reports such tables).
   __device__ __forceinline__ int valid(const Pages& pg, int kb, int t) const {
     const int p = pg.p[t];
     return (kb * 4 + t >= n_table || p < 0 || p >= num_pages) ? 0 : p;

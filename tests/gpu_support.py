@@ -66,9 +66,10 @@ class DecodeSetup:
         def gen(s):
             return s, case.seq_data(s), case.seq_slots(s)
 
+        every = max(8, case.num_seqs // 8)
         with ThreadPoolExecutor(threads) as ex:
             for s, (k, v, q), slots in ex.map(gen, range(case.num_seqs)):
-                if s % 8 == 7:
+                if s % every == every - 1:
                     say(f"    generated and written {s + 1}/{case.num_seqs} sequences")
                 lib.kv_quant_write(up(k), up(v), up(slots), self.cache)
                 vc, vs = quant.quantize_rows(v)

@@ -145,17 +145,6 @@ def test_workspace_too_small_is_rejected():
     assert torch.all(out == 7.0)
 
 
-def test_config5_sampled():
-    need_gpu()
-    case = workloads.config_case(5)
-    say(f"attn_decode config 5: {case.num_seqs} seqs, total ctx {case.total_tokens}, "
-        f"pages {case.num_pages}")
-    order = np.argsort(case.context_lens)
-    keep = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 5, 17, 60})
-    st = DecodeSetup(case, keep=keep)
-    _check_all(st, keep)
-
-
 @pytest.mark.parametrize("n_kv", [1, 3])
 def test_decode_other_kv_head_counts(n_kv):
     need_gpu()

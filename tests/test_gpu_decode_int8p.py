@@ -108,17 +108,6 @@ def test_int8p_rows_before_the_context_are_zero():
     _check(st, out)
 
 
-def test_int8p_config5_sampled():
-    need_gpu()
-    case = workloads.config_case(5)
-    order = np.argsort(case.context_lens)
-    keep = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 5, 17})
-    say(f"attn_decode_int8p config 5: {case.num_seqs} seqs (partition "
-        f"{lib.attn_decode_partition_rows(case.num_seqs, case.max_context_len, 4)})")
-    st = DecodeSetup(case, keep=keep)
-    _check(st, st.run_int8p(), keep)
-
-
 def test_int8p_workspace_checks():
     need_gpu()
     case = workloads.make_decode_case(96, [3000], pages="random")

@@ -46,15 +46,6 @@ def test_prefill_small(ctx, n_new, causal):
     _check(st, np.arange(n_new), causal)
 
 
-def test_prefill_config4_sampled():
-    need_gpu()
-    case = workloads.config_case(4)
-    say(f"attn_prefill_chunk config 4: ctx {case.context_len}, n_new {case.n_new}")
-    st = PrefillSetup(case)
-    rows = np.array([0, 1, 15, 16, 17, 31, 32, 500, 1023, 1024, 1500, 2031, 2046, 2047])
-    _check(st, rows)
-
-
 def test_prefill_rows_match_decode_at_matching_context():
     need_gpu()
     case = workloads.make_prefill_case(60, 2500, 130, k_outliers=4)

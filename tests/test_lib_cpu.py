@@ -303,3 +303,82 @@ def test_attn_prefill_split_workspace_and_validation():
     assert call(fn=L.attn_prefill_chunk_split, args=one) == C["I8A_EINVAL"]  # (out null)
     q8 = [FAKE, None] + base[1:]
     assert call(fn=L.attn_prefill_chunk_split_q8, args=q8) == C["I8A_EINVAL"]  # no q_scales
+
+
+def test_negative_sm_scale_is_refused_on_every_route():
+    # The chunk kernel bounds its running max through the sign of the scale, so every
+    # attention entry point refuses a negative (or non-finite) scale alike.
+    C = _codes()
+    L = m.lib()
+    dec = [FAKE] * 6 + [16, FAKE, 1, 256, 16, 24, 4, 256, -0.0625, FAKE, FAKE, 10 ** 7, None]
+    ver = [FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 63, FAKE, 2, 1000, 200, 24, 4, 256, -0.0625,
+           FAKE, FAKE, 10 ** 8, None]
+    i8p = [FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 63, FAKE, 2, 1000, 200, 24, 4, 256, 0, -0.0625,
+           FAKE, FAKE, 10 ** 8, None]
+    pf = [FAKE, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 1, 16, 24, 4, 256, -0.0625, FAKE, None]
+    sp = [FAKE, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 1, 16, 24, 4, 256, -0.0625, FAKE,
+          FAKE, 10 ** 8, None]
+    cb = [FAKE, FAKE, FAKE, 64, 1, 24, 4, 256, -0.0625, FAKE, None, 0, None]
+    step = [FAKE, FAKE, FAKE, 100, FAKE, FAKE, 64, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, 50, FAKE,
+            100, 24, 4, 256, -0.0625, FAKE, 4096, 10 ** 8, None]
+    for fn, a in ((L.attn_decode, dec), (L.attn_verify, ver), (L.attn_decode_int8p, i8p),
+                  (L.attn_prefill_chunk, pf), (L.attn_prefill_chunk_split, sp),
+                  (L.attn_chunk_bf16, cb), (L.prefill_step, step)):
+        rc, msg = _err(fn(*a))
+        assert rc == C["I8A_EINVAL"] and "sm_scale" in msg, (fn.__name__, rc, msg)
+    # zero is allowed (uniform weights): it gets past the scale check to the null-pointer
+    # check of the missing output
+    a = list(pf)
+    a[13], a[14] = 0.0, None
+    rc, msg = _err(L.attn_prefill_chunk(*a))
+    assert rc == C["I8A_EINVAL"] and "null" in msg
+
+
+def test_check_block_table_names_the_first_bad_entry():
+    import numpy as np
+    C = _codes()
+    table = np.array([[3, 1, 0, 0], [2, 4, 5, 0]], np.int32)
+    ctx = np.array([20, 40], np.int32)               # 2 and 3 blocks used
+    m.check_block_table(table, ctx, 64, 6)          # every used entry in [0, 6)
+    m.check_block_table(table, np.array([0, 40], np.int32), 64, 6)   # context 0 is a padded slot
+    bad = table.copy()
+    bad[1, 2] = 6                                     # out of a pool of 6 pages
+    with pytest.raises(m.Int8AttnError) as e:
+        m.check_block_table(bad, ctx, 64, 6)
+    assert e.value.code == C["I8A_EINVAL"]
+    assert "sequence 1 block 2" in str(e.value) and "page 6" in str(e.value)
+    bad[1, 2] = -1
+    with pytest.raises(m.Int8AttnError, match="page -1"):
+        m.check_block_table(bad, ctx, 64, 6)
+    # an entry past the context is never read and not checked
+    bad = table.copy()
+    bad[0, 3] = 99
+    m.check_block_table(bad, ctx, 64, 6)
+    for c, why in (([20, 65], "above the table's 4 blocks"), ([20, -1], "negative"),
+                   ([20, 40], "above max_context_len")):
+        mc = 30 if why.endswith("max_context_len") else 64
+        with pytest.raises(m.Int8AttnError, match="context"):
+            m.check_block_table(table, np.array(c, np.int32), mc, 6)
+    # one table row for a chunk: context_lens None = one sequence of max_context_len keys
+    m.check_block_table(np.array([5, 0, 2], np.int32), None, 40, 6)
+    with pytest.raises(m.Int8AttnError, match="block 2"):
+        m.check_block_table(np.array([5, 0, 7], np.int32), None, 40, 6)
+    L = m.lib()
+    assert L.int8attn_check_block_table(None, 1, 4, None, 10, 6) == C["I8A_EINVAL"]
+    assert L.int8attn_check_block_table(None, 0, 4, None, 10, 6) == C["I8A_OK"]
+    assert L.int8attn_check_block_table(None, 1, 0, None, 10, 6) == C["I8A_EINVAL"]
+
+
+def test_check_slots():
+    import numpy as np
+    C = _codes()
+    m.check_slots(np.array([0, 17, -1, 95, -5], np.int32), 6)   # pool of 96 slots
+    with pytest.raises(m.Int8AttnError, match="token 2 has slot 96"):
+        m.check_slots(np.array([0, 17, 96], np.int32), 6)
+    with pytest.raises(m.Int8AttnError, match="slot 17 is named by two tokens"):
+        m.check_slots(np.array([17, 3, -1, -1, 17], np.int32), 6)
+    with pytest.raises(TypeError):
+        m.check_slots(np.array([1, 2], np.int64), 6)
+    L = m.lib()
+    assert L.int8attn_check_slots(None, 3, 6) == C["I8A_EINVAL"]
+    assert L.int8attn_check_slots(None, 0, 6) == C["I8A_OK"]
