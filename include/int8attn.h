@@ -465,6 +465,28 @@ int int8attn_check_block_table(const int32_t* block_table, int num_seqs,
  * pass. */
 int int8attn_check_slots(const int32_t* slot_mapping, int n_tokens, int num_pages);
 
+/* ---------------------------------------------------------------------------
+ * Measurement kernels (they compute nothing of the attention method): the measured
+ * ceilings the attention kernels are reported against, timed on the same GPU in the
+ * same run. [R4D "Know your cache regime": a roofline fraction is read against a
+ * ceiling measured in the same cache regime; "When the counters read zero, count the
+ * ISA": a kernel with a known instruction count calibrates the counters.] */
+
+/* int8attn_ceiling_stream_read -- reads `bytes` (a positive multiple of 16; src 16-byte
+ * aligned) once with 16-byte loads, each of n_workgroups workgroups (256 threads) a
+ * contiguous slab, and stores a fold of the bytes to sink[4 * n_workgroups] (uint32, one
+ * word per wave) so that no load is elided. */
+int int8attn_ceiling_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                                 int n_workgroups, void* stream);
+
+/* int8attn_ceiling_mfma_i8 -- n_workgroups workgroups of 8 waves (two per SIMD), each
+ * wave issuing `iters` rounds of 8 independent v_mfma_i32_16x16x64_i8 on register
+ * operands: int8attn_ceiling_mfma_i8_count(...) MFMA instructions of 16 x 16 x 64 MACs
+ * (32,768 int8 ops each) in all. sink: int32 [n_workgroups] (written only in a case that
+ * does not occur; it keeps the results live). */
+int int8attn_ceiling_mfma_i8(int n_workgroups, int iters, int32_t* sink, void* stream);
+int64_t int8attn_ceiling_mfma_i8_count(int n_workgroups, int iters);
+
 #ifdef __cplusplus
 }
 #endif

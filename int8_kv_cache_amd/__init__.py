@@ -21,7 +21,8 @@ __all__ = ["lib", "PagedCache", "alloc_cache", "kv_quant_write", "q_quant", "att
            "attn_prefill_chunk", "attn_prefill_chunk_split",
            "attn_prefill_chunk_split_workspace_bytes", "kv_produce", "attn_chunk_bf16",
            "attn_chunk_bf16_workspace_bytes", "prefill_step",
-           "prefill_step_workspace_bytes", "check_block_table", "check_slots", "Int8AttnError",
+           "prefill_step_workspace_bytes", "check_block_table", "check_slots", "ceiling_stream_read",
+           "ceiling_mfma_i8", "Int8AttnError",
            "HEAD_DIM", "PAGE", "PARTITION", "EXPORTED_SYMBOLS"]
 
 HEAD_DIM = 256
@@ -38,7 +39,8 @@ EXPORTED_SYMBOLS = ("int8attn_last_error", "int8attn_version", "kv_quant_write",
                     "attn_prefill_chunk", "attn_prefill_chunk_split_workspace_bytes",
                     "attn_prefill_chunk_split", "attn_prefill_chunk_split_q8",
                     "attn_chunk_bf16_workspace_bytes", "int8attn_check_block_table",
-                    "int8attn_check_slots")
+                    "int8attn_check_slots", "int8attn_ceiling_stream_read",
+                    "int8attn_ceiling_mfma_i8", "int8attn_ceiling_mfma_i8_count")
 
 _c_void = ctypes.c_void_p
 _c_int = ctypes.c_int
@@ -99,6 +101,9 @@ _SIGNATURES = {
                                           _c_int, _c_float, _c_void, _c_void, _c_size, _c_void]),
     "int8attn_check_block_table": (_c_int, [_c_void, _c_int, _c_int, _c_void, _c_int, _c_int]),
     "int8attn_check_slots": (_c_int, [_c_void, _c_int, _c_int]),
+    "int8attn_ceiling_stream_read": (_c_int, [_c_void, _c_size, _c_void, _c_int, _c_void]),
+    "int8attn_ceiling_mfma_i8": (_c_int, [_c_int, _c_int, _c_void, _c_void]),
+    "int8attn_ceiling_mfma_i8_count": (ctypes.c_int64, [_c_int, _c_int]),
     "attn_prefill_chunk_split_q8": (_c_int, [_c_void, _c_void, _c_int, _c_void, _c_void,
                                              _c_void, _c_void, _c_void, _c_int, _c_int, _c_int,
                                              _c_int, _c_int, _c_int, _c_float, _c_void, _c_void,
@@ -549,3 +554,26 @@ def check_slots(slot_mapping, num_pages: int) -> None:
     raises Int8AttnError for a slot outside the pool or one named by two tokens."""
     s = _host_i32(slot_mapping, "slot_mapping").reshape(-1)
     _check(lib().int8attn_check_slots(s.ctypes.data, s.shape[0], int(num_pages)))
+
+
+def ceiling_stream_read(src: torch.Tensor, n_workgroups: int, sink: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """Measurement kernel: one 16-byte-load pass over src's bytes (the measured read
+    ceiling); returns the sink [4 * n_workgroups] uint32 (as int32)."""
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(4 * n_workgroups, dtype=torch.int32, device=src.device)
+    if sink.numel() < 4 * n_workgroups:
+        raise ValueError("sink needs 4 words per workgroup")
+    _check(lib().int8attn_ceiling_stream_read(_dev(src, "src"), nbytes, _dev(sink, "sink"),
+                                              int(n_workgroups), _stream(stream)))
+    return sink
+
+
+def ceiling_mfma_i8(n_workgroups: int, iters: int, sink: torch.Tensor, stream=None) -> int:
+    """Measurement kernel: a known number of int8 MFMAs (returned) on register operands."""
+    if sink.numel() < n_workgroups:
+        raise ValueError("sink needs one word per workgroup")
+    _check(lib().int8attn_ceiling_mfma_i8(int(n_workgroups), int(iters), _dev(sink, "sink"),
+                                          _stream(stream)))
+    return int(lib().int8attn_ceiling_mfma_i8_count(int(n_workgroups), int(iters)))
