@@ -16,7 +16,8 @@
  * Conventions common to every entry point
  *  - Every pointer argument except `stream` is a DEVICE pointer (hipMalloc'd or
  *    torch-owned GPU memory). The caller owns every buffer; the library keeps no
- *    reference after the call returns and allocates nothing.
+ *    reference after the call returns and allocates nothing (attn_decode_noalloc's
+ *    fixed scratch array is part of the library's own device image).
  *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).
  *    Work is enqueued asynchronously; no call synchronizes.
  *  - Return value: I8A_OK (0) on success, a negative I8A_E* code on error. On an
@@ -434,6 +435,30 @@ int attn_prefill_chunk_split_q8(const int8_t* q_codes, const float* q_scales, in
                                 int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
                                 float sm_scale, float* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_decode_noalloc -- attn_decode for callers that cannot allocate device memory or
+ * pass a workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, kernels and results as attn_decode (bit for bit),
+ * without workspace/workspace_bytes: the split-K partial states go to a fixed device
+ * array inside the library, attn_decode_noalloc_max_bytes() = 32 MiB per GPU (held by
+ * each GPU the library runs on until the process ends; its address is looked up once
+ * per device at the first call there). Nothing is allocated and nothing needs clearing
+ * (every partial that is read was written by the same call).
+ *  - A batch whose partials exceed the array (num_seqs * n_q_heads *
+ *    ceil(max_context_len/512) * 1032 bytes > 32 MiB, e.g. more than 21 sequences at a
+ *    32,768-token context with 24 query heads) returns I8A_EWORKSPACE: use attn_decode.
+ *  - `stream` must belong to the current device (else I8A_EINVAL).
+ *  - Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ *    different streams, or from different threads) race and corrupt each other's
+ *    partials. Order them on one stream. */
+size_t attn_decode_noalloc_max_bytes(void);
+int attn_decode_noalloc(const uint16_t* q,
+                        const int8_t* k_cache, const int8_t* v_cache,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, int max_blocks_per_seq,
+                        const int32_t* context_lens, int num_seqs, int max_context_len,
+                        int num_pages, int n_q_heads, int n_kv_heads, int head_dim,
+                        float sm_scale, float* out, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Opt-in validation of the paging metadata (host arrays).

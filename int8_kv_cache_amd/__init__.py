@@ -21,7 +21,7 @@ __all__ = ["lib", "PagedCache", "alloc_cache", "kv_quant_write", "q_quant", "att
            "attn_prefill_chunk", "attn_prefill_chunk_split",
            "attn_prefill_chunk_split_workspace_bytes", "kv_produce", "attn_chunk_bf16",
            "attn_chunk_bf16_workspace_bytes", "prefill_step",
-           "prefill_step_workspace_bytes", "check_block_table", "check_slots", "ceiling_stream_read",
+           "prefill_step_workspace_bytes", "check_block_table", "check_slots", "ceiling_stream_read", "attn_decode_noalloc",
            "ceiling_mfma_i8", "Int8AttnError",
            "HEAD_DIM", "PAGE", "PARTITION", "EXPORTED_SYMBOLS"]
 
@@ -40,7 +40,8 @@ EXPORTED_SYMBOLS = ("int8attn_last_error", "int8attn_version", "kv_quant_write",
                     "attn_prefill_chunk_split", "attn_prefill_chunk_split_q8",
                     "attn_chunk_bf16_workspace_bytes", "int8attn_check_block_table",
                     "int8attn_check_slots", "int8attn_ceiling_stream_read",
-                    "int8attn_ceiling_mfma_i8", "int8attn_ceiling_mfma_i8_count")
+                    "int8attn_ceiling_mfma_i8", "int8attn_ceiling_mfma_i8_count",
+                    "attn_decode_noalloc", "attn_decode_noalloc_max_bytes")
 
 _c_void = ctypes.c_void_p
 _c_int = ctypes.c_int
@@ -101,6 +102,10 @@ _SIGNATURES = {
                                           _c_int, _c_float, _c_void, _c_void, _c_size, _c_void]),
     "int8attn_check_block_table": (_c_int, [_c_void, _c_int, _c_int, _c_void, _c_int, _c_int]),
     "int8attn_check_slots": (_c_int, [_c_void, _c_int, _c_int]),
+    "attn_decode_noalloc_max_bytes": (_c_size, []),
+    "attn_decode_noalloc": (_c_int, [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void, _c_int,
+                                     _c_void, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                     _c_float, _c_void, _c_void]),
     "int8attn_ceiling_stream_read": (_c_int, [_c_void, _c_size, _c_void, _c_int, _c_void]),
     "int8attn_ceiling_mfma_i8": (_c_int, [_c_int, _c_int, _c_void, _c_void]),
     "int8attn_ceiling_mfma_i8_count": (ctypes.c_int64, [_c_int, _c_int]),
@@ -577,3 +582,25 @@ def ceiling_mfma_i8(n_workgroups: int, iters: int, sink: torch.Tensor, stream=No
     _check(lib().int8attn_ceiling_mfma_i8(int(n_workgroups), int(iters), _dev(sink, "sink"),
                                           _stream(stream)))
     return int(lib().int8attn_ceiling_mfma_i8_count(int(n_workgroups), int(iters)))
+
+
+def attn_decode_noalloc(q: torch.Tensor, cache, block_table: torch.Tensor,
+                        context_lens: torch.Tensor, max_context_len: int, out: torch.Tensor,
+                        sm_scale: float | None = None, stream=None) -> torch.Tensor:
+    """attn_decode without a workspace (the library's fixed per-GPU scratch array holds the
+    partials); `out` [S, Hq, 256] fp32 must be given, so nothing is allocated here either."""
+    if q.dim() != 3 or q.dtype != torch.bfloat16:
+        raise TypeError("q must be bfloat16 [S, Hq, head_dim]")
+    S, Hq, D = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_table must be [S, max_blocks] and context_lens [S]")
+    if out.shape != (S, Hq, D):
+        raise ValueError("out must be [S, Hq, head_dim]")
+    sm = float(sm_scale if sm_scale is not None else D ** -0.5)
+    _check(lib().attn_decode_noalloc(_dev(q, "q"), *cache.ptrs(),
+                                     _dev(block_table, "block_table", torch.int32),
+                                     block_table.shape[1],
+                                     _dev(context_lens, "context_lens", torch.int32), S,
+                                     int(max_context_len), cache.num_pages, Hq, cache.n_kv_heads,
+                                     D, sm, _dev(out, "out", torch.float32), _stream(stream)))
+    return out

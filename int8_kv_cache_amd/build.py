@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libint8attn.so")
 SOURCES = ["api.hip", "quant_write.hip", "decode.hip", "decode_i8pv.hip", "prefill.hip",
-           "chunk_bf16.hip", "ceilings.hip"]
+           "chunk_bf16.hip", "ceilings.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

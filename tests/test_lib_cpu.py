@@ -382,3 +382,16 @@ def test_check_slots():
     L = m.lib()
     assert L.int8attn_check_slots(None, 3, 6) == C["I8A_EINVAL"]
     assert L.int8attn_check_slots(None, 0, 6) == C["I8A_OK"]
+
+
+def test_attn_decode_noalloc_limits_on_the_host():
+    # the size check comes before any HIP call, so it runs without a GPU
+    C = _codes()
+    L = m.lib()
+    assert m.lib().attn_decode_noalloc_max_bytes() == 32 << 20
+    base = [FAKE] * 6 + [2048, FAKE, 22, 32768, 2048, 24, 4, 256, 0.0625, FAKE, None]
+    rc, msg = _err(L.attn_decode_noalloc(*base))      # 22 x 24 x 64 x 1032 B > 32 MiB
+    assert rc == C["I8A_EWORKSPACE"] and "attn_decode" in msg
+    a = list(base)
+    a[8] = 0
+    assert L.attn_decode_noalloc(*a) == C["I8A_OK"]   # no sequences: no-op
