@@ -73,6 +73,14 @@ __device__ __forceinline__ float col_sum(float v) {
   return a + b;
 }
 
+// col_max for values whose bit patterns order like the values (non-negative floats).
+__device__ __forceinline__ uint32_t col_max_u(uint32_t v) {
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  const uint32_t a = max(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  return max(r[0], r[1]);
+}
+
 // Whole-wave max / sum without LDS: DPP inside each 16-lane row, then the row swaps.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -19,9 +19,11 @@
 //    Row r of tile t is token 4t + r%4 of page r/4, so lane group gq (lanes 16gq..)
 //    ends up holding all 16 tokens of page gq for one query row: its P codes, in token
 //    order, are then exactly the B operand that meets page gq's dim-major V bytes;
-//  * x = qk * sK * (sQ * sm_scale * log2 e), online max with a lazy rescale (the
-//    reference max only moves when a block max exceeds it by more than 2^8, so
-//    p <= 256);
+//  * x = qk * sK * (sQ * sm_scale * log2 e), online softmax with a lazy rescale: the
+//    weights p = 2^(x - m) are taken against the running reference max m as it stands,
+//    and only when a lane's block sum of them passes 2^8 (or the row has no m yet) is
+//    the block redone with its max, m moving only if that max exceeds it by more than
+//    2^8; so p <= 256, and the common block takes no max of the scores at all;
 //  * w = p * sV, per (row, block) s_b = max w / 127, codes rint(w / s_b) in [0, 127]
 //    (one fma onto 1.5 * 2^23 rounds each to an integer in the low mantissa bits, two
 //    byte permutes pack four); the denominator sums the unquantized p;
@@ -49,13 +51,15 @@ constexpr int kPfPage = kBlockBytes + 64;  // LDS stride of a staged K page: the
                                            // block start on different banks (V pages are
                                            // read one page per lane group and need none)
 
-// Moves one 64-key block (4 pages of K and of V, 32 KB) of KV head g into an LDS buffer
-// with direct global->LDS loads (global_load_lds_dwordx4: lane i of a wave lands at
-// LDS base + 16 i), 1 KB per wave instruction. Wave w < 8 moves quarter w % 4 of every
-// page of K (w < 4) or V; K page t lands at t * kPfPage, V page t at t * 4096. Waves 8 and 9 move the 64 K / V
-// token scales (global_load_lds_dword, lane = key). Nothing waits here: the loads land
-// while the previous block is computed and are waited for once, before the barrier.
-// Page ids are fetched into scalar registers one block before their loads.
+// Moves one 64-key block (4 pages of K and of V, 32 KB, and their 128 token scales) of
+// KV head g into an LDS buffer with direct global->LDS loads. Wave w moves page t = w % 4
+// of the block: waves 0-3 its 4 KB of K codes, waves 4-7 its 4 KB of V codes (four 1 KB
+// wave loads, global_load_lds_dwordx4: lane i lands at LDS base + 16 i), waves 8-11 its 16
+// K and 16 V scales (global_load_lds_dword on lanes 0-15). So every wave resolves one
+// page id per block (one scalar load, fetched a block ahead) and the work of issuing is
+// spread over all twelve waves. K page t lands at t * kPfPage, V page t at t * 4096.
+// Nothing waits here: the loads land while the previous block is computed and are waited
+// for once, before the barrier.
 struct BlockLoader {
   const int8_t* k_cache;
   const int8_t* v_cache;
@@ -64,49 +68,39 @@ struct BlockLoader {
   const int32_t* block_table;
   int n_table, num_pages, n_kv_heads, g, w, lane;
 
-  struct Pages { int p[4]; };
-
-  // Raw table entries of block kb (the index is clamped; validity is checked at use).
-  __device__ __forceinline__ Pages pages(int kb) const {
-    Pages r;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) r.p[t] = block_table[min(kb * 4 + t, n_table - 1)];
-    return r;
+  // This wave's raw table entry for block kb. The index is clamped to the table, so a
+  // block past the context reads the sequence's last page, whose keys are masked.
+  __device__ __forceinline__ int page(int kb) const {
+    return block_table[min(kb * 4 + (w & 3), n_table - 1)];
   }
-  // Entries past the context read page 0, and their keys are masked. An entry outside
-  // the pool inside the context also reads page 0, whose keys then enter the result: it
-  // is memory-safe but wrong (int8attn_check_block_table reports such tables).
-  __device__ __forceinline__ int valid(const Pages& pg, int kb, int t) const {
-    const int p = pg.p[t];
-    return (kb * 4 + t >= n_table || p < 0 || p >= num_pages) ? 0 : p;
-  }
-  __device__ __forceinline__ void issue(const Pages& pg, int kb, int8_t (*kv_lds)[4 * kPfPage],
+  // An entry outside the pool reads page 0 instead: memory-safe but wrong when it lies
+  // inside the context (int8attn_check_block_table reports such tables).
+  __device__ __forceinline__ void issue(int p_raw, int8_t (*kv_lds)[4 * kPfPage],
                                         float (*sc_lds)[64]) const {
+    const int t = w & 3;
+    const int p = (uint32_t)p_raw < (uint32_t)num_pages ? p_raw : 0;
     if (w < 8) {
-      const int kv = w >> 2, quarter = w & 3;
-      const int8_t* cache = kv ? v_cache : k_cache;
+      const int kv = w >> 2;
+      const int8_t* src = (kv ? v_cache : k_cache) + ((size_t)p * n_kv_heads + g) * kBlockBytes;
+      int8_t* dst = &kv_lds[kv][t * (kv ? kBlockBytes : kPfPage)];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const size_t off = ((size_t)valid(pg, kb, t) * n_kv_heads + g) * kBlockBytes + quarter * 1024;
-        const int8_t* wave_src = cache + off;  // uniform; the lane offset stays 32-bit
-        uint32_t lo = lane * 16;
+      for (int qq = 0; qq < 4; ++qq) {
+        uint32_t lo = lane * 16 + qq * 1024;
         asm volatile("" : "+v"(lo));  // keeps (scalar base, 32-bit lane offset) addressing
         __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(wave_src + lo),
-            (__attribute__((address_space(3))) void*)&kv_lds[kv][t * (kv ? kBlockBytes : kPfPage) + quarter * 1024],
-            16, 0, 0);
+            (const __attribute__((address_space(1))) void*)(src + lo),
+            (__attribute__((address_space(3))) void*)(dst + qq * 1024), 16, 0, 0);
       }
-    } else if (w < 10) {  // K scales (wave 8) or V scales (wave 9); lane = key 16t + o
-      const int t = lane >> 4;
-      const int p0 = valid(pg, kb, 0), p1 = valid(pg, kb, 1), p2 = valid(pg, kb, 2),
-                p3 = valid(pg, kb, 3);
-      const int page = t == 0 ? p0 : t == 1 ? p1 : t == 2 ? p2 : p3;
+    } else if (lane < 16) {
       // 32-bit element index: the launcher checks num_pages * n_kv_heads * 16 < 2^32.
-      const uint32_t off = ((uint32_t)page * (uint32_t)n_kv_heads + (uint32_t)g) * kPage + (lane & 15);
-      const float* src = (w == 9 ? v_scale : k_scale) + off;
-      asm volatile("" : "+v"(src));  // computed here, not kept live across the loop
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)&sc_lds[w - 8][0],
+      const uint32_t off = ((uint32_t)p * (uint32_t)n_kv_heads + (uint32_t)g) * kPage;
+      uint32_t lo = lane;
+      asm volatile("" : "+v"(lo));
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(k_scale + off + lo),
+                                       (__attribute__((address_space(3))) void*)&sc_lds[0][16 * t],
+                                       4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(v_scale + off + lo),
+                                       (__attribute__((address_space(3))) void*)&sc_lds[1][16 * t],
                                        4, 0, 0);
     }
   }
@@ -137,87 +131,118 @@ struct RowState {
 // Without key partitions every row sees key 0 in its first block.
 template <int GUARD>
 __device__ __forceinline__ void block_step(
-    int kb, int nkb, const BlockLoader& ld, BlockLoader::Pages& pg_next, const RowCtx& rc,
+    int kb, int nkb, const BlockLoader& ld, int& pg_next, const RowCtx& rc,
     RowState& st, const int8_t* sK, const int8_t* sV, const float* sSk, const float* sSv,
     int8_t (*nKV)[4 * kPfPage], float (*nSc)[64]) {
   // QK: S[t] rows = tokens 4t..4t+3 of each of the 4 pages. The operands of group u+1
   // are read while the products of group u run.
   v4i S[4];
+  auto qk = [&]() {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) S[t] = v4i{0, 0, 0, 0};
-  v4i ka[4], qa;
+    for (int t = 0; t < 4; ++t) S[t] = v4i{0, 0, 0, 0};
+    v4i ka[4], qa;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) ka[t] = *reinterpret_cast<const v4i*>(sK + rc.koff + t * 64);
-  qa = rc.qB[0];
+    for (int t = 0; t < 4; ++t) ka[t] = *reinterpret_cast<const v4i*>(sK + rc.koff + t * 64);
+    qa = rc.qB[0];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    v4i kn[4], qn;
-    if (u < 3) {
+    for (int u = 0; u < 4; ++u) {
+      v4i kn[4], qn;
+      if (u < 3) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) kn[t] = *reinterpret_cast<const v4i*>(sK + rc.koff + (u + 1) * 1024 + t * 64);
-      qn = rc.qB[u + 1];
+        for (int t = 0; t < 4; ++t) kn[t] = *reinterpret_cast<const v4i*>(sK + rc.koff + (u + 1) * 1024 + t * 64);
+        qn = rc.qB[u + 1];
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) S[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[t], qa, S[t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (u < 3) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ka[t] = kn[t];
+        qa = qn;
+      }
     }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) S[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[t], qa, S[t], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (u < 3) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) ka[t] = kn[t];
-      qa = qn;
-    }
-  }
+  };
+  qk();
   // The next block's loads go out once this block's query reads are issued.
   if (kb + 1 < nkb) {
-    ld.issue(pg_next, kb + 1, nKV, nSc);
-    pg_next = ld.pages(kb + 2);
+    ld.issue(pg_next, nKV, nSc);
+    pg_next = ld.page(kb + 2);
   }
   // y = qk * sK (key 16gq + 4t + i of the block), masked on diagonal / tail blocks only.
   const int key0 = kb * 64;
   const bool need_mask = (key0 + 64 > rc.kfull) || (key0 + 64 > rc.ctx);
   float y[16], sv[16];
+  auto scores = [&]() {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const float4 sk = *reinterpret_cast<const float4*>(&sSk[16 * rc.gq + 4 * t]);
-    const float4 vs = *reinterpret_cast<const float4*>(&sSv[16 * rc.gq + 4 * t]);
-    y[4 * t] = (float)S[t][0] * sk.x;
-    y[4 * t + 1] = (float)S[t][1] * sk.y;
-    y[4 * t + 2] = (float)S[t][2] * sk.z;
-    y[4 * t + 3] = (float)S[t][3] * sk.w;
-    sv[4 * t] = vs.x; sv[4 * t + 1] = vs.y; sv[4 * t + 2] = vs.z; sv[4 * t + 3] = vs.w;
+    for (int t = 0; t < 4; ++t) {
+      const float4 sk = *reinterpret_cast<const float4*>(&sSk[16 * rc.gq + 4 * t]);
+      const float4 vs = *reinterpret_cast<const float4*>(&sSv[16 * rc.gq + 4 * t]);
+      y[4 * t] = (float)S[t][0] * sk.x;
+      y[4 * t + 1] = (float)S[t][1] * sk.y;
+      y[4 * t + 2] = (float)S[t][2] * sk.z;
+      y[4 * t + 3] = (float)S[t][3] * sk.w;
+      sv[4 * t] = vs.x; sv[4 * t + 1] = vs.y; sv[4 * t + 2] = vs.z; sv[4 * t + 3] = vs.w;
+    }
+    if (need_mask) {  // diagonal or context-tail block (wave-uniform)
+      // Masked keys (including slots past the context, whose scales are not data) get
+      // y = -inf and sV = 0, so their weight is exactly 0.
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (key0 + 16 * rc.gq + e >= rc.lim) {
+          y[e] = -INFINITY;
+          sv[e] = 0.f;
+        }
+    }
+  };
+  scores();
+  // Weights against the running max as it stands: no block max is taken on this path.
+  // The lane's sum of the block's weights then shows whether a score passed the running
+  // max by more than the lazy window (a weight above 2^8 makes the sum exceed it; a row
+  // with no reference max yet gives a non-finite sum): only then is the block redone on
+  // the exact path, with the block max and the rescale. Both paths produce the same
+  // weights whenever no rescale is due, so the result does not depend on the path.
+  float wm = 0.f, lb = 0.f;
+  bool exact = __any(st.m_run == -INFINITY);
+  if (!exact) {
+    const float nm0 = -st.m_run;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(y[e], rc.rs, nm0));
+      lb += p;
+      y[e] = p * sv[e];
+      wm = fmaxf(wm, y[e]);
+    }
+    exact = __any(!(lb <= (float)(1 << (int)kLazyRescale)));
   }
-  if (need_mask) {  // diagonal or context-tail block (wave-uniform)
-    // Masked keys (including slots past the context, whose scales are not data) get
-    // y = -inf and sV = 0, so their weight is exactly 0.
+  if (exact) {  // first block of a row, or a score beyond the lazy window: recompute
+    qk();
+    scores();
+    float ymax = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (key0 + 16 * rc.gq + e >= rc.lim) {
-        y[e] = -INFINITY;
-        sv[e] = 0.f;
-      }
+    for (int e = 0; e < 16; ++e) ymax = fmaxf(ymax, y[e]);
+    const float xmax = ymax * rc.rs;
+    if (__any(xmax > st.m_run + kLazyRescale)) {
+      const float m_new = fmaxf(st.m_run, col_max(xmax));
+      const float alpha = (GUARD && m_new == st.m_run) ? 1.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) st.acc[dt] *= alpha;
+      st.l_part *= alpha;
+      st.corr *= alpha;
+      st.m_run = m_new;
+    }
+    const float nm = (GUARD && st.m_run == -INFINITY) ? 0.f : -st.m_run;
+    wm = 0.f;
+    lb = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(y[e], rc.rs, nm));
+      lb += p;
+      y[e] = p * sv[e];
+      wm = fmaxf(wm, y[e]);
+    }
   }
-  float ymax = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) ymax = fmaxf(ymax, y[e]);
-  const float xmax = ymax * rc.rs;
-  if (__any(xmax > st.m_run + kLazyRescale)) {
-    const float m_new = fmaxf(st.m_run, col_max(xmax));
-    const float alpha = (GUARD && m_new == st.m_run) ? 1.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
-#pragma unroll
-    for (int dt = 0; dt < 16; ++dt) st.acc[dt] *= alpha;
-    st.l_part *= alpha;
-    st.corr *= alpha;
-    st.m_run = m_new;
-  }
-  const float nm = (GUARD && st.m_run == -INFINITY) ? 0.f : -st.m_run;
-  float wm = 0.f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const float p = __builtin_amdgcn_exp2f(fmaf(y[e], rc.rs, nm));
-    st.l_part += p;
-    y[e] = p * sv[e];
-    wm = fmaxf(wm, y[e]);
-  }
-  wm = col_max(wm);
+  st.l_part += lb;
+  wm = __uint_as_float(col_max_u(__float_as_uint(wm)));  // wm >= 0: integer order
   // 127 / wm via the hardware reciprocal (about 1 ulp): a code can move only at an
   // exact rounding tie, and w * inv stays below 127.5, so codes never exceed 127.
   // fma(w, inv, 1.5 * 2^23) lies in [2^23, 2^24), where the fp32 spacing is 1, so its
@@ -349,9 +374,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_chunk_kernel(
 
   const BlockLoader ld{k_cache, v_cache, k_scale, v_scale, block_table, (ctx + kPage - 1) / kPage,
                        num_pages, n_kv_heads, g, w, lane};
-  BlockLoader::Pages pg_next = ld.pages(kb0);
-  if (nkb > kb0) ld.issue(pg_next, kb0, s_kv0, s_sc0);  // first block in flight during the Q work
-  pg_next = ld.pages(kb0 + 1);
+  int pg_next = ld.page(kb0);
+  if (nkb > kb0) ld.issue(pg_next, s_kv0, s_sc0);  // first block in flight during the Q work
+  pg_next = ld.page(kb0 + 1);
 
   // ---- quantize this wave's 16 query rows (head h); rows past the chunk are zero.
   int8_t* qrows = &s_q[hl * kPfTok + 16 * half][0];
