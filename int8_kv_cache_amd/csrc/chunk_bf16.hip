@@ -10,7 +10,8 @@
 // block (double buffered; the next block's K and V move by direct global->LDS loads while
 // the current one is computed):
 //  * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (exact bf16 products, fp32 sums): tile t
-//    holds keys 16t..16t+15 of the block; the query operands stay in registers;
+//    holds keys 16t..16t+15 of the block; the query operands stay in registers, and the
+//    K operands of the next 32-dim group are read while the current group's products run;
 //  * online softmax in the exp2 domain with the lazy rescale (the reference max moves
 //    only when a block max exceeds it by more than 2^8);
 //  * out^T += V^T . P^T on v_mfma_f32_16x16x32_bf16 with P carried as two bf16 terms,
@@ -20,7 +21,7 @@
 //    consecutive keys that each lane already holds from two tiles (key index 8 kg + j =
 //    key 16(2h + j/4) + 4 kg + j%4), so P needs no lane movement; V is staged as key rows
 //    by direct-to-LDS loads and read with gfx950's transposing LDS read (ds_read_b64_tr_b16),
-//    two per operand.
+//    two per operand, one dim tile ahead of the products.
 #include <algorithm>
 
 #include "common.hpp"
@@ -92,22 +93,38 @@ struct RowState {
 __device__ __forceinline__ void block_step(int kb, int nkb, const Loader& ld, const v8bf* qop,
                                            int my_tok, int first_tok, bool causal, int n,
                                            float qk_scale_log2,
-                                           int gq, int nn, const int* vaddr, RowState& st,
+                                           int gq, int nn, int vbase, RowState& st,
                                            Block cur, Block nxt) {
   const bool more = kb + 1 < nkb;
   if (more) {
-    ld.issue_k(kb + 1, nxt.k);
     ld.issue_v(kb + 1, nxt.v);
+    ld.issue_k(kb + 1, nxt.k);
   }
-  // S^T tile t: rows = keys 16t..16t+15 (lane (m, kg) reads key 16t + m, dims 32u + 8kg..)
+  // S^T tile t: rows = keys 16t..16t+15 (lane (m, kg) reads key 16t + m, dims 32u + 8kg..).
+  // Dim group u feeds the 4 tiles' independent accumulations; the operands of group u + 1
+  // are read while the products of group u run.
   v4f S[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    S[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 4; ++t) S[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  {
+    const int8_t* kp = cur.k + gq * 1024 + nn * 16;
+    v8bf ka[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ka[t] = *reinterpret_cast<const v8bf*>(kp + t * 256);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const v8bf a = *reinterpret_cast<const v8bf*>(cur.k + (4 * u + gq) * 1024 + (16 * t + nn) * 16);
-      S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[u], S[t], 0, 0, 0);
+      v8bf kn[4];
+      if (u < 7) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kn[t] = *reinterpret_cast<const v8bf*>(kp + (u + 1) * 4096 + t * 256);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t], qop[u], S[t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (u < 7) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ka[t] = kn[t];
+      }
     }
   }
   // Lane (nn, gq) holds keys 64kb + 16t + 4gq + i of its query row. Only blocks that
@@ -164,20 +181,38 @@ __device__ __forceinline__ void block_step(int kb, int nkb, const Loader& ld, co
   // and 32h + 16 + 4gq..+3 (tiles 2h and 2h + 1). Two transposed 8-byte reads give them:
   // within each 16-lane group, lane s addresses 4 dims (16dt + 4(s & 3)..) of key row
   // 32h (+16) + 4gq + s/4, and lane nn receives element nn & 3 of lanes nn/4 + 4k.
+  // The operands of dim tile dt + 1 are read while the 4 products of tile dt run.
+  int vb = vbase;
+  asm volatile("" : "+v"(vb));  // the 8 offsets vb ^ 32dt are formed here, not kept live
+  auto vop = [&](int dt, int h) {
+    const int8_t* p0 = cur.v + (vb ^ ((dt & 7) << 5)) + (dt >> 3) * 256 + 32 * h * 512;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s*)(p0));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s*)(p0 + 16 * 512));
+    return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  v8bf va[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) va[h] = vop(0, h);
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) {
+    v8bf vn[2];
+    if (dt < 15) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) vn[h] = vop(dt + 1, h);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int8_t* p0 = cur.v + vaddr[dt & 7] + (dt >> 3) * 256 + 32 * h * 512;
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s*)(p0));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s*)(p0 + 16 * 512));
-      const v8bf a = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, ph[h]),
+      st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[h], __builtin_bit_cast(v8bf, ph[h]),
                                                            st.acc[dt], 0, 0, 0);
-      st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, pl[h]),
+      st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[h], __builtin_bit_cast(v8bf, pl[h]),
                                                            st.acc[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (dt < 15) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) va[h] = vn[h];
     }
   }
   if (more) __builtin_amdgcn_s_waitcnt(0);  // the next K/V block has landed in LDS
@@ -235,33 +270,35 @@ __global__ __launch_bounds__(kCbThreads, 1) void chunk_bf16_kernel(
   const int nkb = SPLIT ? min(nkb_tile, kb0 + sp.part_blocks) : nkb_tile;
   if (SPLIT && kb0 >= nkb) return;  // the tile's keys end before this partition
 
+  // Four distinct LDS variables, so that the compiler can tell the in-flight direct-to-LDS
+  // writes of one buffer from the reads of the other and need not wait for them. The V
+  // buffers carry the names that sort first: the compiler lays the kernel's LDS variables
+  // out in name order, which puts them in the low 64 KB, where every transposed V read
+  // reaches its buffer through the instruction's 16-bit offset field (an add per read
+  // otherwise).
+  __shared__ __align__(16) int8_t sv0[kVBytes];
+  __shared__ __align__(16) int8_t sv1[kVBytes];
   __shared__ __align__(16) int8_t s_k0[kKBytes];
   __shared__ __align__(16) int8_t s_k1[kKBytes];
-  __shared__ __align__(16) int8_t s_v0[kVBytes];
-  __shared__ __align__(16) int8_t s_v1[kVBytes];
 
   const Loader ld{k, v, n, n_kv_heads, g, w, lane};
   {
+    ld.issue_v(kb0, sv0);
     ld.issue_k(kb0, s_k0);
-    ld.issue_v(kb0, s_v0);
     // Query operands: lane (nn, gq) holds dims 32u + 8gq..+7 of its row (rows past the
     // chunk re-read the last one; their outputs are not stored).
     v8bf qop[8];
     const size_t qrow = ((size_t)min(my_tok, n - 1) * n_q_heads + h) * kHeadDim;
 #pragma unroll
     for (int u = 0; u < 8; ++u) qop[u] = *reinterpret_cast<const v8bf*>(q + qrow + 32 * u + 8 * gq);
-    // Byte offsets of this lane's transposed V reads for dim tiles dt = 0..7 (tiles 8..15
-    // add 256): key row 4gq + nn/4 (+32h, +16 as immediates), dims 16dt + 4(nn & 3), with
-    // the row's chunk swizzle (row & 7 = (4gq + nn/4) & 7 for every h and half).
-    int vaddr[8];
-    {
-      const int r = 4 * gq + (nn >> 2), swz = (r & 7) << 1;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const int c = 2 * d + ((nn & 3) >> 1);
-        vaddr[d] = r * 512 + (c ^ swz) * 16 + (nn & 1) * 8;
-      }
-    }
+    // Byte offset of this lane's transposed V reads for dim tile dt (0..7; tiles 8..15
+    // add 256): key row r = 4gq + nn/4 (+32h, +16 as immediates), dims 16dt + 4(nn & 3),
+    // 16-byte chunk 2dt + (nn & 3)/2 stored at chunk (2dt + (nn & 3)/2) ^ 2(r & 7), i.e.
+    // vbase ^ 32dt with vbase the offset for dt = 0.
+    const int vbase = [&] {
+      const int r = 4 * gq + (nn >> 2);
+      return r * 512 + (r & 7) * 32 + ((nn & 3) >> 1) * 16 + (nn & 1) * 8;
+    }();
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
 
@@ -270,12 +307,12 @@ __global__ __launch_bounds__(kCbThreads, 1) void chunk_bf16_kernel(
     st.l_part = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) st.acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
-    const Block b0{s_k0, s_v0}, b1{s_k1, s_v1};
+    const Block b0{s_k0, sv0}, b1{s_k1, sv1};
     for (int kb = kb0; kb < nkb; kb += 2) {
-      block_step(kb, nkb, ld, qop, my_tok, t0, causal != 0, n, qk_scale_log2, gq, nn, vaddr, st,
+      block_step(kb, nkb, ld, qop, my_tok, t0, causal != 0, n, qk_scale_log2, gq, nn, vbase, st,
                  b0, b1);
       if (kb + 1 < nkb)
-        block_step(kb + 1, nkb, ld, qop, my_tok, t0, causal != 0, n, qk_scale_log2, gq, nn, vaddr,
+        block_step(kb + 1, nkb, ld, qop, my_tok, t0, causal != 0, n, qk_scale_log2, gq, nn, vbase,
                    st, b1, b0);
     }
     const float l = col_sum(st.l_part);
