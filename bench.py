@@ -344,6 +344,11 @@ def main():
     # the streaming read's workgroup count is the best of a short sweep (a ceiling)
     read_wg = min((512, 1024, 2048, 4096), key=lambda n: per_call_eager(
         lambda: [lib.ceiling_stream_read(b, n, sink) for b in read_bufs * 2], 2 * R))
+    # the page-gather read (the decode's own access pattern): pages per workgroup likewise
+    n_blk = -(-ctx // 16)
+    gather_ppw = min((8, 16, 32), key=lambda n: per_call_eager(
+        lambda: [lib.ceiling_page_gather(c, table, n_blk, n, sink) for c in copies * 2], 2 * R))
+    gather_b = n_blk * (dec.n_kv_heads * (2 * 4096 + 2 * 64) + 4)
     mfma_wg, mfma_iters = 1024, 2000
     mfma_count = lib.lib().int8attn_ceiling_mfma_i8_count(mfma_wg, mfma_iters)
 
@@ -355,6 +360,8 @@ def main():
         "read_decode_size": (lambda: [lib.ceiling_stream_read(b, read_wg, sink)
                                       for _ in range(rounds) for b in read_bufs], rounds * R),
         "read_1GiB": (lambda: lib.ceiling_stream_read(big, 4096, sink), 1),
+        "page_gather": (lambda: [lib.ceiling_page_gather(c, table, n_blk, gather_ppw, sink)
+                                 for _ in range(rounds) for c in copies], rounds * R),
         "mfma_i8": (lambda: lib.ceiling_mfma_i8(mfma_wg, mfma_iters, sink), 1),
     }
     graphs = {name: (capture(fn), n) for name, (fn, n) in work.items()}
@@ -373,6 +380,7 @@ def main():
     rd_us, rd_reps = trimmed(reps["read_decode_size"])
     big_us, _ = trimmed(reps["read_1GiB"])
     mf_us, mf_reps = trimmed(reps["mfma_i8"])
+    ga_us, ga_reps = trimmed(reps["page_gather"])
     read_ceiling = dec_b / (rd_us * 1e-6) / 1e9          # GB/s for the decode's bytes
     read_1g = (1 << 30) / (big_us * 1e-6) / 1e9
     mfma_ceiling = mfma_count * MFMA_I8_OPS / (mf_us * 1e-6) / 1e12
@@ -427,12 +435,18 @@ def main():
             "stream_read_decode_size_reps_us": rd_reps,
             "stream_read_workgroups": read_wg,
             "stream_read_1GiB_GBps": round(read_1g, 1),
+            "page_gather_decode_us": round(ga_us, 3),
+            "page_gather_decode_GBps": round(gather_b / (ga_us * 1e-6) / 1e9, 1),
+            "page_gather_decode_reps_us": ga_reps,
+            "page_gather_pages_per_workgroup": gather_ppw,
             "mfma_i8_TOPS": round(mfma_ceiling, 1),
             "mfma_i8_reps_us": mf_reps,
             "mfma_i8_count": int(mfma_count),
             "note": "library kernels int8attn_ceiling_stream_read (16-byte loads, the decode's "
-                    "68 MB over 8 rotating buffers, MALL-cold) and int8attn_ceiling_mfma_i8 "
-                    "(8 independent v_mfma_i32_16x16x64_i8 chains per wave), same protocol"},
+                    "68 MB over 8 rotating buffers, MALL-cold), int8attn_ceiling_page_gather "
+                    "(the decode's K/V pages and scales through its block table, over the same "
+                    "cache copies) and int8attn_ceiling_mfma_i8 (8 independent "
+                    "v_mfma_i32_16x16x64_i8 chains per wave), same protocol"},
         "roofline": {"bound": "mfma", "kernel": "prefill_chunk_kernel",
                      "achieved": round(pf_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
                      "frac": round(pf_tops / INT8_PEAK_TOPS, 4),
@@ -444,6 +458,7 @@ def main():
                             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                             "frac_of_measured": round(dec_gbps / read_ceiling, 4),
                             "measured_peak": round(read_ceiling, 1),
+                            "frac_of_page_gather": round(ga_us / dec_us, 4),
                             "per_launch": dec_b, "traffic": recorded_traffic("decode")},
     }
 

@@ -504,6 +504,20 @@ int int8attn_check_slots(const int32_t* slot_mapping, int n_tokens, int num_page
 int int8attn_ceiling_stream_read(const void* src, size_t bytes, uint32_t* sink,
                                  int n_workgroups, void* stream);
 
+/* int8attn_ceiling_page_gather -- reads, for each of the first n_blocks entries of the
+ * block table (device int32; entries outside [0, num_pages) read page 0), the 4 KB of K
+ * codes and the 4 KB of V codes of every KV head and their 16 + 16 scales, from caches laid
+ * out as for attn_decode: the decode's access pattern without its arithmetic. One
+ * workgroup of 256 threads per (run of pages_per_workgroup pages, KV head); sink (device)
+ * receives 4 words per workgroup: 4 * ceil(n_blocks / pages_per_workgroup) * n_kv_heads
+ * uint32. Bytes read: n_blocks * (n_kv_heads * (2 * 4096 + 2 * 64) + 4).
+ * Errors: I8A_EINVAL for a null pointer or a count <= 0 (nothing enqueued). */
+int int8attn_ceiling_page_gather(const int8_t* k_cache, const int8_t* v_cache,
+                                 const float* k_scale, const float* v_scale,
+                                 const int32_t* block_table, int n_blocks, int n_kv_heads,
+                                 int num_pages, int pages_per_workgroup, uint32_t* sink,
+                                 void* stream);
+
 /* int8attn_ceiling_mfma_i8 -- n_workgroups workgroups of 8 waves (two per SIMD), each
  * wave issuing `iters` rounds of 8 independent v_mfma_i32_16x16x64_i8 on register
  * operands: int8attn_ceiling_mfma_i8_count(...) MFMA instructions of 16 x 16 x 64 MACs

@@ -22,7 +22,7 @@ __all__ = ["lib", "PagedCache", "alloc_cache", "kv_quant_write", "q_quant", "att
            "attn_prefill_chunk_split_workspace_bytes", "kv_produce", "attn_chunk_bf16",
            "attn_chunk_bf16_workspace_bytes", "prefill_step",
            "prefill_step_workspace_bytes", "check_block_table", "check_slots", "ceiling_stream_read", "attn_decode_noalloc",
-           "ceiling_mfma_i8", "Int8AttnError",
+           "ceiling_mfma_i8", "ceiling_page_gather", "Int8AttnError",
            "HEAD_DIM", "PAGE", "PARTITION", "EXPORTED_SYMBOLS"]
 
 HEAD_DIM = 256
@@ -41,6 +41,7 @@ EXPORTED_SYMBOLS = ("int8attn_last_error", "int8attn_version", "kv_quant_write",
                     "attn_chunk_bf16_workspace_bytes", "int8attn_check_block_table",
                     "int8attn_check_slots", "int8attn_ceiling_stream_read",
                     "int8attn_ceiling_mfma_i8", "int8attn_ceiling_mfma_i8_count",
+                    "int8attn_ceiling_page_gather",
                     "attn_decode_noalloc", "attn_decode_noalloc_max_bytes")
 
 _c_void = ctypes.c_void_p
@@ -109,6 +110,7 @@ _SIGNATURES = {
     "int8attn_ceiling_stream_read": (_c_int, [_c_void, _c_size, _c_void, _c_int, _c_void]),
     "int8attn_ceiling_mfma_i8": (_c_int, [_c_int, _c_int, _c_void, _c_void]),
     "int8attn_ceiling_mfma_i8_count": (ctypes.c_int64, [_c_int, _c_int]),
+    "int8attn_ceiling_page_gather": (_c_int, [_c_void] * 5 + [_c_int] * 4 + [_c_void, _c_void]),
     "attn_prefill_chunk_split_q8": (_c_int, [_c_void, _c_void, _c_int, _c_void, _c_void,
                                              _c_void, _c_void, _c_void, _c_int, _c_int, _c_int,
                                              _c_int, _c_int, _c_int, _c_float, _c_void, _c_void,
@@ -573,6 +575,21 @@ def ceiling_stream_read(src: torch.Tensor, n_workgroups: int, sink: torch.Tensor
     _check(lib().int8attn_ceiling_stream_read(_dev(src, "src"), nbytes, _dev(sink, "sink"),
                                               int(n_workgroups), _stream(stream)))
     return sink
+
+
+def ceiling_page_gather(cache, block_table: torch.Tensor, n_blocks: int,
+                        pages_per_workgroup: int, sink: torch.Tensor, stream=None) -> int:
+    """Measurement kernel: the decode's reads (K and V codes and scales of the first n_blocks
+    pages of a block-table row, every KV head) without its arithmetic; returns the bytes
+    read."""
+    n_kv = cache.n_kv_heads
+    nx = -(-int(n_blocks) // int(pages_per_workgroup))
+    if sink.numel() < 4 * nx * n_kv:
+        raise ValueError("sink needs 4 words per workgroup")
+    _check(lib().int8attn_ceiling_page_gather(
+        *cache.ptrs(), _dev(block_table, "block_table", torch.int32), int(n_blocks), n_kv,
+        int(cache.num_pages), int(pages_per_workgroup), _dev(sink, "sink"), _stream(stream)))
+    return int(n_blocks) * (n_kv * (2 * 4096 + 2 * 64) + 4)
 
 
 def ceiling_mfma_i8(n_workgroups: int, iters: int, sink: torch.Tensor, stream=None) -> int:

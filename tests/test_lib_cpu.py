@@ -199,9 +199,10 @@ def test_kv_produce_and_q8_validation():
     cb = [FAKE, FAKE, FAKE, 64, 2, 24, 4, 256, 0.0625, FAKE, None, 0, None]
     assert L.attn_chunk_bf16(*cb) == C["I8A_EINVAL"]    # causal flag
     # bf16 chunk split: 2,048 causal rows = 1,056 key blocks per KV head over 64 tiles;
-    # x 4 heads / 256 CUs -> 17 blocks per partition, 2 partitions, rows 1,088.. merged
+    # x 4 heads / 256 CUs -> 17 blocks per CU, partitions of 17 * 6 / 5 = 20 blocks,
+    # 2 partitions, rows 1,280.. merged
     cws = m.attn_chunk_bf16_workspace_bytes
-    assert cws(2048, True, 24, 4) == (2048 - 1088) * 24 * 2 * 258 * 4
+    assert cws(2048, True, 24, 4) == (2048 - 1280) * 24 * 2 * 258 * 4
     assert cws(2048, False, 24, 4) == 0                 # non-causal: one pass
     assert cws(64, True, 24, 4) == 0                    # one key block
     need = cws(2048, True, 24, 4)
