@@ -477,6 +477,11 @@ def main():
         g = capture(lambda: [call() for _ in range(n_calls)])
         return per_call_us(g.replay, n_calls)
 
+    # the chunk's writer without the launch gaps of an eager call (8 calls per graph)
+    qw_graph_us = graph_us(lambda: lib.kv_quant_write(k_chunk, v_chunk, s_chunk, pcache), n_calls=8)
+    res["quant_write_2048_us_graph"] = round(qw_graph_us, 3)
+    res["quant_write_GBps_graph"] = round(qw_b / (qw_graph_us * 1e-6) / 1e9, 1)
+
     res["decode_us_mall_warm"] = round(per_call_us(
         lambda: [lib.attn_decode(q_dec, base, table, ctx_t, ctx, out=out_dec, workspace=ws)
                  for _ in range(R)], R), 3)
@@ -584,8 +589,12 @@ def next_rows(res, lib, torch, dev, up, bf16, dec, pf, copies, table, ctx_t, ctx
                           reps=20)
     one = (qb[-1:], kb[-1:], vb[-1:], pos_t[-1:], rope_tab, s_chunk[-1:], pcache)
     tok1 = graph_us(lambda: lib.kv_produce(*one), n_calls=8)
+    prod_graph_us = graph_us(lambda: lib.kv_produce(qb, kb, vb, pos_t, rope_tab, s_chunk, pcache),
+                             n_calls=8)
     res["produce_2048"] = {"us": round(prod_us, 3), "bytes": prod_bytes,
                            "hbm_GBps": round(prod_bytes / (prod_us * 1e-6) / 1e9, 1),
+                           "us_graph": round(prod_graph_us, 3),
+                           "hbm_GBps_graph": round(prod_bytes / (prod_graph_us * 1e-6) / 1e9, 1),
                            "one_token_us_graph": round(tok1, 3)}
     # the high-precision route of a chunk with no history: bf16 attention of the chunk's
     # 2,048 rotated rows over themselves (causal)
