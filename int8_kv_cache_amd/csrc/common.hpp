@@ -95,8 +95,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Row quantizer for one row of 256 values spread over a wave, 4 per lane (lane l holds
 // elements 4l..4l+3). Rule: amax = max|x|, scale = amax/127 (IEEE fp32 division),
-// code = clamp(rint(x/scale), -127, 127) with x/scale an IEEE division and rint half
-// to even; scale == 0 gives all-zero codes. Returns the 4 codes packed little-endian.
+// code = clamp(rint(x/scale), -127, 127) with x/scale the correctly rounded quotient and
+// rint half to even; scale == 0 gives all-zero codes. Returns the 4 codes packed
+// little-endian. The quotient is formed by a reciprocal multiply wherever that provably
+// rounds to the same code, and by the IEEE division elsewhere (below).
 // ("INT8 KV and INT8 MMAC attention on a gfx936 DCU", §2.1.)
 __device__ __forceinline__ uint32_t quantize4(float x0, float x1, float x2, float x3,
                                               float* scale_out) {
@@ -105,12 +107,31 @@ __device__ __forceinline__ uint32_t quantize4(float x0, float x1, float x2, floa
   const float scale = amax / 127.0f;
   *scale_out = scale;
   if (scale == 0.0f) return 0u;
-  auto q = [scale](float x) -> uint32_t {
-    float r = rintf(x / scale);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (uint32_t)((int)r) & 0xffu;
-  };
-  return q(x0) | (q(x1) << 8) | (q(x2) << 16) | (q(x3) << 24);
+  // |x / scale| <= 127 (1 + 2^-23), so the codes need no clamp, and rint(v) of such a v
+  // is fl(v + 1.5 * 2^23) - 1.5 * 2^23, whose fp32 bits carry the code's two's complement
+  // in their low byte. y = x * rcp(scale) lies within 2^-22 |y| of the correctly rounded
+  // x / scale, so the two round to the same integer unless y is that close to a
+  // half-integer; only then (and with a denormal scale, whose reciprocal is not finite)
+  // does the lane divide.
+  constexpr float kM = 12582912.0f;  // 1.5 * 2^23
+  const float x[4] = {x0, x1, x2, x3};
+  float t[4];
+  bool slow = !(scale >= 0x1p-126f);
+  const float r = __builtin_amdgcn_rcpf(scale);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float y = x[i] * r;
+    t[i] = y + kM;
+    const float e = y - (t[i] - kM);  // exact: y minus its nearest integer
+    slow |= fabsf(e) >= fmaf(fabsf(y), -0x1p-20f, 0.5f);
+  }
+  if (slow) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = x[i] / scale + kM;
+  }
+  const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(t[1]), __float_as_uint(t[0]), 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(t[3]), __float_as_uint(t[2]), 0x04000c0cu);
+  return lo | hi;
 }
 
 // Four signed int8 codes (one dword) -> their exact values as fp16, in two halves of

@@ -36,22 +36,37 @@ __device__ __forceinline__ float rot_second(float b, float c, float a, float s) 
 #pragma clang fp contract(off)
   return b * c + a * s;
 }
-__device__ __forceinline__ void rope4(float* x, const float* __restrict__ cs, int rd, int lane) {
+// The cos/sin of one token for this lane's 4 dims (loaded once, used for K and every
+// query row of the token), and the lane holding the partner dims.
+struct RopeLane {
+  float cc[4], ss[4];
+  int partner;
+  bool in, first;
+};
+__device__ __forceinline__ RopeLane rope_lane(const float* __restrict__ cs, int rd, int lane) {
+  RopeLane r;
   const int half = rd >> 1;
   const int d0 = lane * 4;
-  const bool in = d0 < rd, first = d0 < half;
-  const int partner = in ? (first ? lane + (half >> 2) : lane - (half >> 2)) : lane;
-  float y[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) y[j] = __shfl(x[j], partner);
-  if (in) {
-    const int i0 = first ? d0 : d0 - half;
+  r.in = d0 < rd;
+  r.first = d0 < half;
+  r.partner = r.in ? (r.first ? lane + (half >> 2) : lane - (half >> 2)) : lane;
+  if (r.in) {
+    const int i0 = r.first ? d0 : d0 - half;
     const float4 c = *reinterpret_cast<const float4*>(cs + i0);
     const float4 sn = *reinterpret_cast<const float4*>(cs + half + i0);
-    const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+    r.cc[0] = c.x; r.cc[1] = c.y; r.cc[2] = c.z; r.cc[3] = c.w;
+    r.ss[0] = sn.x; r.ss[1] = sn.y; r.ss[2] = sn.z; r.ss[3] = sn.w;
+  }
+  return r;
+}
+__device__ __forceinline__ void rope4(float* x, const RopeLane& r) {
+  float y[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) y[j] = __shfl(x[j], r.partner);
+  if (r.in) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      x[j] = first ? rot_first(x[j], cc[j], y[j], ss[j]) : rot_second(x[j], cc[j], y[j], ss[j]);
+      x[j] = r.first ? rot_first(x[j], r.cc[j], y[j], r.ss[j]) : rot_second(x[j], r.cc[j], y[j], r.ss[j]);
   }
 }
 
@@ -135,14 +150,14 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
                            qx[PRODUCE ? i : 0][hh]);
     }
   }
-  const float* cs_row[TPW] = {};  // RoPE rows of the tokens
+  RopeLane rl[PRODUCE ? TPW : 1];  // RoPE of the tokens
   if (PRODUCE && pr.rotary_dim > 0) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int t = min(tok0 + TPW * w + i, n_tokens - 1);
       const int pos = min(max(pr.positions[t], 0), pr.max_pos - 1);  // clamped: memory-safe
-      cs_row[i] = pr.cos_sin + (size_t)pos * pr.rotary_dim;
-      rope4(kx[i], cs_row[i], pr.rotary_dim, lane);
+      rl[PRODUCE ? i : 0] = rope_lane(pr.cos_sin + (size_t)pos * pr.rotary_dim, pr.rotary_dim, lane);
+      rope4(kx[i], rl[PRODUCE ? i : 0]);
     }
   }
   if (PRODUCE && pr.k_rot != nullptr) {
@@ -168,7 +183,7 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
 #pragma unroll
       for (int hh = 0; hh < kGroup; ++hh) {
         float* xr = qx[PRODUCE ? i : 0][hh];
-        if (pr.rotary_dim > 0) rope4(xr, cs_row[i], pr.rotary_dim, lane);
+        if (pr.rotary_dim > 0) rope4(xr, rl[PRODUCE ? i : 0]);
         const size_t row = (size_t)t * pr.n_q_heads + head * kGroup + hh;
         if (pr.q_rot != nullptr) store_bf16x4(pr.q_rot + row * kHeadDim + lane * 4, xr);
         if (pr.q_codes != nullptr) {
