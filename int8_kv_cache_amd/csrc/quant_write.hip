@@ -117,14 +117,15 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
   __shared__ __align__(16) uint32_t s_v[kBlockBytes / 4];  // V block [dim][token]
   __shared__ float s_sc[2][16];
 
-  if (w == 0) {  // page-run test on the group's 16 slots (lanes 16..63 repeat 0..15)
-    const int t = tok0 + (lane & 15);
-    const int sl = t < n_tokens ? slots[t] : -1;
-    const int s0 = __shfl(sl, 0);
-    const bool ok = t < n_tokens && sl == s0 + (lane & 15) && (s0 & 15) == 0 && s0 >= 0 &&
-                    (long long)s0 + 15 < n_slots;
-    const bool all = __all(ok);
-    if (lane == 0) s_run = all ? 1 : 0;
+  // Positions first, so that the RoPE rows they address can be requested right after the
+  // K/V rows: the rotation of K waits for them, and for every load issued before them.
+  int posn[PRODUCE ? TPW : 1];
+  if (PRODUCE && pr.rotary_dim > 0) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = min(tok0 + TPW * w + i, n_tokens - 1);
+      posn[PRODUCE ? i : 0] = min(max(pr.positions[t], 0), pr.max_pos - 1);  // clamped: memory-safe
+    }
   }
   float kx[TPW][4], vx[TPW][4];
   int myslot[TPW];
@@ -135,6 +136,14 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
     load_row4<IN_BF16>(k, row, lane, kx[i]);
     load_row4<IN_BF16>(v, row, lane, vx[i]);
     myslot[i] = tok0 + TPW * w + i < n_tokens ? slots[tok0 + TPW * w + i] : -1;
+  }
+  // The RoPE rows of the tokens, ahead of the query rows in the load order.
+  RopeLane rl[PRODUCE ? TPW : 1];
+  if (PRODUCE && pr.rotary_dim > 0) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+      rl[PRODUCE ? i : 0] = rope_lane(pr.cos_sin + (size_t)posn[PRODUCE ? i : 0] * pr.rotary_dim,
+                                      pr.rotary_dim, lane);
   }
   // Query rows of the group for this wave's tokens, loaded with the K/V rows (one round
   // trip); tokens past the batch re-read the last one and are not stored.
@@ -150,15 +159,15 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
                            qx[PRODUCE ? i : 0][hh]);
     }
   }
-  RopeLane rl[PRODUCE ? TPW : 1];  // RoPE of the tokens
+  // The group's 16 slots for the page-run test (wave 0), consumed only before the writes.
+  int sl_run = -1, s0_run = -1;
+  if (w == 0) {
+    const int t = tok0 + (lane & 15);
+    sl_run = t < n_tokens ? slots[t] : -1;
+  }
   if (PRODUCE && pr.rotary_dim > 0) {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int t = min(tok0 + TPW * w + i, n_tokens - 1);
-      const int pos = min(max(pr.positions[t], 0), pr.max_pos - 1);  // clamped: memory-safe
-      rl[PRODUCE ? i : 0] = rope_lane(pr.cos_sin + (size_t)pos * pr.rotary_dim, pr.rotary_dim, lane);
-      rope4(kx[i], rl[PRODUCE ? i : 0]);
-    }
+    for (int i = 0; i < TPW; ++i) rope4(kx[i], rl[PRODUCE ? i : 0]);
   }
   if (PRODUCE && pr.k_rot != nullptr) {
 #pragma unroll
@@ -167,6 +176,7 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
       if (t < n_tokens) store_bf16x4(pr.k_rot + ((size_t)t * n_kv_heads + head) * kHeadDim + lane * 4, kx[i]);
     }
   }
+  if (w == 0) s0_run = __shfl(sl_run, 0);
   uint32_t kq[TPW], vq[TPW];
   float ks[TPW], vs[TPW];
 #pragma unroll
@@ -194,6 +204,13 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
         }
       }
     }
+  }
+  if (w == 0) {  // page-run test on the group's 16 slots (lanes 16..63 repeat 0..15)
+    const int t = tok0 + (lane & 15);
+    const bool ok = t < n_tokens && sl_run == s0_run + (lane & 15) && (s0_run & 15) == 0 &&
+                    s0_run >= 0 && (long long)s0_run + 15 < n_slots;
+    const bool all = __all(ok);
+    if (lane == 0) s_run = all ? 1 : 0;
   }
   __syncthreads();
   if (s_run) {
