@@ -128,3 +128,43 @@ def test_page_runs_and_scattered_slots_in_one_call(in_bf16):
     k = rng.standard_normal((T, H, 256), dtype=np.float32) * np.float32(2.5)
     v = rng.standard_normal((T, H, 256), dtype=np.float32)
     _write_and_compare(k, v, slots, num_pages=17, H=H, in_bf16=in_bf16)
+
+
+def test_scales_across_binades_bit_exact():
+    # Rows whose scales span 2^-125 .. 2^120 (every binade of a normal scale, and the first
+    # denormal ones just below 2^-126) with random mantissas, plus rows whose elements sit
+    # on and next to half-integer multiples of the scale at each magnitude: the codes come
+    # from a reciprocal multiply away from rounding ties and from the IEEE division near
+    # them, and both must give the rule's codes everywhere.
+    need_gpu()
+    rng = np.random.default_rng(17)
+    n_rows = 4 * 512
+    exps = np.concatenate([np.arange(-125, 121), np.array([-127, -128, -130, -126])])
+    e = exps[rng.integers(0, exps.size, n_rows)]
+    amax = np.ldexp(1.0 + rng.random(n_rows), e).astype(np.float32) * np.float32(127.0)
+    rows = (rng.uniform(-1.0, 1.0, (n_rows, 256)) * amax[:, None]).astype(np.float32)
+    # half the rows: elements at (k + 1/2) * scale, nudged by -1, 0, +1 ulp
+    half = rows[: n_rows // 2]
+    sc = (amax[: n_rows // 2] / np.float32(127.0)).astype(np.float32)
+    kk = rng.integers(-126, 126, half.shape).astype(np.float32)
+    tie = ((kk + np.float32(0.5)) * sc[:, None]).astype(np.float32)
+    nudge = rng.integers(-1, 2, half.shape)
+    tie = np.where(nudge > 0, np.nextafter(tie, np.float32(np.inf)),
+                   np.where(nudge < 0, np.nextafter(tie, np.float32(-np.inf)), tie)).astype(np.float32)
+    keep = np.abs(tie) < amax[: n_rows // 2, None]
+    half[keep] = tie[keep]
+    rows[np.arange(n_rows), rng.integers(0, 256, n_rows)] = amax     # the row's amax is exact
+    finite = np.isfinite(rows).all(axis=1)
+    assert finite.all()
+    say(f"kv_quant_write: {n_rows} rows, scale exponents {int(e.min())}..{int(e.max())}")
+    k = rows.reshape(n_rows // 4, 4, 256)
+    v = rows[::-1].copy().reshape(n_rows // 4, 4, 256)
+    slots = rng.permutation(64 * 16)[: n_rows // 4].astype(np.int32)
+    _write_and_compare(k, v, slots, 64, 4)
+    # the same rows as bf16 query rows through q_quant
+    qb = workloads.f32_to_bf16_bits(rows)
+    codes, scales = lib.q_quant(bf16_tensor(qb.reshape(n_rows // 4, 4, 256)))
+    torch.cuda.synchronize()
+    rc, rs = quant.quantize_rows(quant.bf16_bits_to_f32(qb))
+    assert np.array_equal(codes.cpu().numpy().reshape(n_rows, 256), rc)
+    assert np.array_equal(scales.cpu().numpy().reshape(n_rows).view(np.uint32), rs.view(np.uint32))

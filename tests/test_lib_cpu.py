@@ -396,3 +396,39 @@ def test_attn_decode_noalloc_limits_on_the_host():
     a = list(base)
     a[8] = 0
     assert L.attn_decode_noalloc(*a) == C["I8A_OK"]   # no sequences: no-op
+
+
+def test_reciprocal_code_tie_band():
+    # The kernels take each code as rint(x * r), r the hardware reciprocal of the scale
+    # (within one ulp of 1 / scale), unless y = x * r lies within 2^-20 |y| of a
+    # half-integer, where they use the IEEE quotient x / scale. Checked here in numpy for
+    # reciprocals one ulp below, at and one ulp above the correctly rounded one: every
+    # element whose code from y differs from rint(x / scale) lies inside that band, on
+    # rows built to sit on and next to rounding ties at scales across the normal range.
+    import numpy as np
+    rng = np.random.default_rng(23)
+    n_rows = 3000
+    e = rng.integers(-125, 121, n_rows)
+    amax = (np.ldexp(1.0 + rng.random(n_rows), e) * 127.0).astype(np.float32)
+    rows = (rng.uniform(-1.0, 1.0, (n_rows, 256)) * amax[:, None]).astype(np.float32)
+    sc = (amax / np.float32(127.0)).astype(np.float32)
+    kk = rng.integers(-126, 126, rows.shape).astype(np.float32)
+    tie = ((kk + np.float32(0.5)) * sc[:, None]).astype(np.float32)
+    nudge = rng.integers(-1, 2, rows.shape)
+    tie = np.where(nudge > 0, np.nextafter(tie, np.float32(np.inf)),
+                   np.where(nudge < 0, np.nextafter(tie, np.float32(-np.inf)), tie)).astype(np.float32)
+    keep = (np.abs(tie) < amax[:, None]) & (rng.random(rows.shape) < 0.5)
+    rows[keep] = tie[keep]
+    rows[np.arange(n_rows), rng.integers(0, 256, n_rows)] = amax
+    scale = (np.abs(rows).max(axis=1) / np.float32(127.0)).astype(np.float32)
+    assert np.all(scale >= np.float32(2.0 ** -126))
+    q_div = np.rint(rows / scale[:, None])
+    r0 = (np.float32(1.0) / scale).astype(np.float32)
+    misrounded = 0
+    for r in (np.nextafter(r0, np.float32(0)), r0, np.nextafter(r0, np.float32(np.inf))):
+        y = (rows * r.astype(np.float32)[:, None]).astype(np.float32)
+        band = np.abs(np.abs(y - np.rint(y)) - np.float32(0.5)) <= np.abs(y) * np.float32(2.0 ** -20)
+        wrong = np.rint(y) != q_div
+        assert not np.any(wrong & ~band)
+        misrounded += int(wrong.sum())
+    assert misrounded > 1000   # the rows do reach the ties a plain reciprocal gets wrong
