@@ -528,6 +528,58 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def gpu_shares(lib, torch, dev, up, dec, copies, table, ctx, q_dec, graph_us):
+    """Config 3's decode at one GPU's share of a sharded run, at the share's real shape:
+    tensor parallel over 4 GPUs (one KV head and its 6 query heads, all 32,768 keys) and
+    context parallel over 8 GPUs (4,096 of the keys, 8 partitions, all heads; the exchange
+    and the cross-GPU merge are not part of it). MALL-cold: every call in a replay reads
+    its own K/V (24 one-head caches of 17 MB; 64 disjoint 4,096-key windows of the 8 cache
+    copies), graph-timed. The one-head K/V are drawn on the GPU (torch's generator), N(0,1)
+    as in config 3."""
+    import itertools
+    D, page = dec.head_dim, workloads.PAGE
+    t = np.arange(ctx)
+    slots = up((dec.block_table[0, t // page].astype(np.int64) * page + t % page).astype(np.int32))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(dec.seed + 100)
+    tp = []
+    for _ in range(24):
+        c1 = lib.alloc_cache(dec.num_pages, 1, dev)
+        lib.kv_quant_write(torch.randn((ctx, 1, D), generator=gen, device=dev),
+                           torch.randn((ctx, 1, D), generator=gen, device=dev), slots, c1)
+        tp.append(c1)
+    q_tp = q_dec[:, :6].contiguous()
+    ctx1 = torch.full((1,), ctx, dtype=torch.int32, device=dev)
+    o_tp = torch.empty((1, 6, D), dtype=torch.float32, device=dev)
+    w_tp = torch.empty(lib.attn_decode_workspace_bytes(1, ctx, 6), dtype=torch.uint8, device=dev)
+    it = itertools.cycle(tp)
+    us_tp = graph_us(lambda: lib.attn_decode(q_tp, next(it), table, ctx1, ctx, out=o_tp,
+                                             workspace=w_tp), n_calls=len(tp))
+    b_tp = decode_bytes(ctx, 6, 1, D)
+    n_cp = 4096
+    wins = [(c, up(np.ascontiguousarray(dec.block_table[:, w * (n_cp // page):(w + 1) * (n_cp // page)])))
+            for c in copies for w in range(ctx // n_cp)]
+    ctx_cp = torch.full((1,), n_cp, dtype=torch.int32, device=dev)
+    o_cp = torch.empty((1, dec.n_q_heads, D), dtype=torch.float32, device=dev)
+    w_cp = torch.empty(lib.attn_decode_workspace_bytes(1, n_cp, dec.n_q_heads), dtype=torch.uint8,
+                       device=dev)
+    it2 = itertools.cycle(wins)
+
+    def cp_call():
+        c, tb = next(it2)
+        lib.attn_decode(q_dec, c, tb, ctx_cp, n_cp, out=o_cp, workspace=w_cp)
+    us_cp = graph_us(cp_call, n_calls=len(wins))
+    b_cp = decode_bytes(n_cp, dec.n_q_heads, dec.n_kv_heads, D)
+    del tp
+    return {"tp4_1kv_6q_ctx32768": {"us": round(us_tp, 3), "bytes": b_tp,
+                                    "hbm_GBps": round(b_tp / (us_tp * 1e-6) / 1e9, 1),
+                                    "workgroups": ctx // 512},
+            "cp8_4096_keys_4kv_24q": {"us": round(us_cp, 3), "bytes": b_cp,
+                                      "hbm_GBps": round(b_cp / (us_cp * 1e-6) / 1e9, 1),
+                                      "workgroups": (n_cp // 512) * dec.n_kv_heads},
+            "note": "graph-timed, MALL-cold; one GPU's share of config 3's decode"}
+
+
 def next_rows(res, lib, torch, dev, up, bf16, dec, pf, copies, table, ctx_t, ctx, q_dec, out_dec,
               ws, dec_b, q_pf, pcache, ptable, out_pf, k4, v4, slots4, s_chunk, pos0, per_call_us,
               graph_us):
@@ -555,6 +607,8 @@ def next_rows(res, lib, torch, dev, up, bf16, dec, pf, copies, table, ctx_t, ctx
                                                       workspace=ws8))
     res["decode_int8p_ctx32768"] = {"us": round(i8p_us, 3), "partition": part,
                                     "hbm_GBps": round(dec_b / (i8p_us * 1e-6) / 1e9, 1)}
+    res["decode_one_gpu_shares"] = gpu_shares(lib, torch, dev, up, dec, copies, table, ctx,
+                                              q_dec, graph_us)
     # short chunks at the end of the prefill context (the last n query rows): the split
     # route (key partitions + merge, or the int8-P decode kernel for n <= 8) against the
     # one pass; both stream the whole int8 K/V of the head group
