@@ -129,7 +129,11 @@ __global__ __launch_bounds__(512, 1) void split_i8pv_flat_kernel(
     int tid_item = tid0;
     asm volatile("" : "+v"(tid_item));
     const int tid = tid_item, lane = tid & 63;
-    const int w = w0;
+    // (likewise the wave index, so that the per-row conditions derived from it are
+    // recomputed per item as scalar compares instead of flags kept, and spilled, across it)
+    int w_item = w0;
+    asm volatile("" : "+s"(w_item));
+    const int w = w_item;
 #include "decode_i8pv_item.inc"
   };
   const int stride = (num_seqs + 63) / 64;  // <= 16 for kFlatMaxSeqs sequences
