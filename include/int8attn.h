@@ -19,7 +19,10 @@
  *    reference after the call returns and allocates nothing (attn_decode_noalloc's
  *    fixed scratch array is part of the library's own device image).
  *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).
- *    Work is enqueued asynchronously; no call synchronizes.
+ *    Work is enqueued asynchronously; no call synchronizes. A call enqueues only kernel
+ *    launches (no memset, copy or host callback), so it may be captured into a HIP
+ *    graph; every replay recomputes the outputs from the inputs it then finds, bit for
+ *    bit as an eager call does (no kernel uses atomics or timing-dependent orders).
  *  - Return value: I8A_OK (0) on success, a negative I8A_E* code on error. On an
  *    argument error nothing is enqueued and no output is touched. The message of the
  *    last error on the calling thread is available from int8attn_last_error().
