@@ -119,13 +119,14 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
 
   // Positions first, so that the RoPE rows they address can be requested right after the
   // K/V rows: the rotation of K waits for them, and for every load issued before them.
+  // Only the load is here, its first use (the clamp) comes after the row loads; the load is
+  // unconditional (no rotation: a slot is read instead, unused) so that it shares a block
+  // with the row loads and the compiler does not wait for it before issuing them.
   int posn[PRODUCE ? TPW : 1];
-  if (PRODUCE && pr.rotary_dim > 0) {
+  if (PRODUCE) {
+    const int32_t* ppos = pr.rotary_dim > 0 ? pr.positions : slots;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int t = min(tok0 + TPW * w + i, n_tokens - 1);
-      posn[PRODUCE ? i : 0] = min(max(pr.positions[t], 0), pr.max_pos - 1);  // clamped: memory-safe
-    }
+    for (int i = 0; i < TPW; ++i) posn[PRODUCE ? i : 0] = ppos[min(tok0 + TPW * w + i, n_tokens - 1)];
   }
   float kx[TPW][4], vx[TPW][4];
   int myslot[TPW];
@@ -141,9 +142,10 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
   RopeLane rl[PRODUCE ? TPW : 1];
   if (PRODUCE && pr.rotary_dim > 0) {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i)
-      rl[PRODUCE ? i : 0] = rope_lane(pr.cos_sin + (size_t)posn[PRODUCE ? i : 0] * pr.rotary_dim,
-                                      pr.rotary_dim, lane);
+    for (int i = 0; i < TPW; ++i) {
+      const int pos = min(max(posn[PRODUCE ? i : 0], 0), pr.max_pos - 1);  // clamped: memory-safe
+      rl[PRODUCE ? i : 0] = rope_lane(pr.cos_sin + (size_t)pos * pr.rotary_dim, pr.rotary_dim, lane);
+    }
   }
   // Query rows of the group for this wave's tokens, loaded with the K/V rows (one round
   // trip); tokens past the batch re-read the last one and are not stored.
