@@ -162,7 +162,7 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
     }
   }
   // The group's 16 slots for the page-run test (wave 0), consumed only before the writes.
-  int sl_run = -1, s0_run = -1;
+  int sl_run = -1;
   if (w == 0) {
     const int t = tok0 + (lane & 15);
     sl_run = t < n_tokens ? slots[t] : -1;
@@ -178,7 +178,6 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
       if (t < n_tokens) store_bf16x4(pr.k_rot + ((size_t)t * n_kv_heads + head) * kHeadDim + lane * 4, kx[i]);
     }
   }
-  if (w == 0) s0_run = __shfl(sl_run, 0);
   uint32_t kq[TPW], vq[TPW];
   float ks[TPW], vs[TPW];
 #pragma unroll
@@ -209,6 +208,7 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
   }
   if (w == 0) {  // page-run test on the group's 16 slots (lanes 16..63 repeat 0..15)
     const int t = tok0 + (lane & 15);
+    const int s0_run = __shfl(sl_run, 0);
     const bool ok = t < n_tokens && sl_run == s0_run + (lane & 15) && (s0_run & 15) == 0 &&
                     s0_run >= 0 && (long long)s0_run + 15 < n_slots;
     const bool all = __all(ok);
