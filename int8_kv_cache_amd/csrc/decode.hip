@@ -162,13 +162,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   const int keys = max(0, ctx - nq + qi + 1);  // keys this query row sees
   const int P = (keys + part_rows - 1) / part_rows;
   float* o = out + ((size_t)z * n_q_heads + h) * kHeadDim;
-  if (P == 0) {
-    o[d] = 0.f;
-    return;
-  }
   __shared__ __align__(16) float s_a[64];  // the chunk's partition weights, broadcast
   float M = -INFINITY, L = 0.f, acc = 0.f;
-  for (int j0 = 0; j0 < P; j0 += 64) {
+  // The first chunk is merged whatever P is (P = 0: every weight 0, output 0 below): with
+  // no exit before it, its loads are issued together with the context length's instead of
+  // after it.
+  for (int j0 = 0; j0 == 0 || j0 < P; j0 += 64) {
     const int cnt = min(64, P - j0);
     if (j0 > 0) {
       __syncthreads();  // the previous chunk's weights have been read
@@ -193,7 +192,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     acc = acc * r + sacc;
     M = cm;
   }
-  o[d] = acc / L;
+  o[d] = P > 0 ? acc / L : 0.f;
 }
 
 int launch_decode(const void* q, const float* q_scales, const int8_t* k_cache, const int8_t* v_cache,
