@@ -7,8 +7,8 @@
 //
 // Workgroup = (32 query tokens, KV head g): 12 waves = the 6 query heads of the group x
 // two 16-token halves, every K/V byte staged once in LDS for 192 query rows. Per 64-key
-// block (double buffered; the next block's K and V move by direct global->LDS loads while
-// the current one is computed):
+// block (double buffered; the next block's K and V move by direct global->LDS buffer loads
+// while the current one is computed):
 //  * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (exact bf16 products, fp32 sums): tile t
 //    holds keys 16t..16t+15 of the block; the query operands stay in registers, and the
 //    K operands of the next 32-dim group are read while the current group's products run;
@@ -21,7 +21,9 @@
 //    consecutive keys that each lane already holds from two tiles (key index 8 kg + j =
 //    key 16(2h + j/4) + 4 kg + j%4), so P needs no lane movement; V is staged as key rows
 //    by direct-to-LDS loads and read with gfx950's transposing LDS read (ds_read_b64_tr_b16),
-//    two per operand, one dim tile ahead of the products.
+//    two per operand, one dim tile ahead of the products;
+//  * the row's weight sum on the matrix core as well: ones . P^T over the same hi and lo
+//    terms, so the sum and the weighted values see the same weights.
 #include <algorithm>
 
 #include "common.hpp"
@@ -47,44 +49,51 @@ struct Block {
   int8_t* v;   // staged V block (kVBytes)
 };
 
-// Loads of key block kb by direct-to-LDS dword x4 loads: K as instruction c = dim chunk
-// c of 8 dims, lane = key; V as key rows. Keys past the chunk re-read the last one (they
-// are masked).
+// Loads of key block kb by direct-to-LDS buffer loads (dword x4): K as instruction c =
+// dim chunk c of 8 dims, lane = key; V as key rows, two keys per instruction. The
+// block's address and bound are scalar: the resource starts at key 64 kb of head g and
+// ends after the chunk's last key row, so the rows past the chunk read as zeros (their
+// weights are 0). Each lane keeps one offset per operand.
 struct Loader {
   const uint16_t* k;
   const uint16_t* v;
-  int n, n_kv_heads, g, w, lane;
+  int n, n_kv_heads, g, w;
+  uint32_t rstride;  // bytes per key row (all KV heads)
+  uint32_t k_vo;     // key = lane
+  uint32_t v_vo;     // key 2i + half (the 2i rows go in the scalar offset), swizzled chunk
 
-  __device__ __forceinline__ size_t row(int kb) const {
-    const int key = min(kb * 64 + lane, n - 1);
-    return ((size_t)key * n_kv_heads + g) * kHeadDim;
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t* base, int kb) const {
+    const char* p = reinterpret_cast<const char*>(base) +
+                    ((size_t)kb * 64 * n_kv_heads + g) * (kHeadDim * 2);
+    const uint32_t rows = (uint32_t)min(n - kb * 64, 64);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0,
+                                             (int)((rows - 1) * rstride + kHeadDim * 2),
+                                             0x00020000);
   }
   __device__ __forceinline__ void issue_k(int kb, int8_t* k_lds) const {
-    const size_t r = row(kb);
+    const __amdgpu_buffer_rsrc_t r = rsrc(k, kb);
     for (int c = w; c < 32; c += kCbWaves)
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(k + r + c * 8),
-          (__attribute__((address_space(3))) void*)(k_lds + c * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(k_lds + c * 1024), 16, k_vo, c * 16, 0, 0);
   }
-  // V rows (512 B per key) by direct-to-LDS dword x4 loads, two keys per instruction
-  // (instruction i = keys 2i, 2i+1). The 16-byte chunks of key row r are stored XOR-ed
-  // with (r & 7) << 1: LDS chunk c of row r holds dims 8 (c ^ ((r & 7) << 1)) .. +7, so
-  // the transposed reads of 16 rows at one dim range spread over all banks.
+  // V rows (512 B per key), instruction i = keys 2i, 2i+1. The 16-byte chunks of key row
+  // r are stored XOR-ed with (r & 7) << 1: LDS chunk c of row r holds dims
+  // 8 (c ^ ((r & 7) << 1)) .. +7, so the transposed reads of 16 rows at one dim range
+  // spread over all banks. A wave's instructions i = w + 12 j all have r & 7 = (2w + half) & 7.
   __device__ __forceinline__ void issue_v(int kb, int8_t* v_lds) const {
-    const int half = lane >> 5, c = lane & 31;
-    for (int i = w; i < 32; i += kCbWaves) {
-      const int r = 2 * i + half;
-      const int key = min(kb * 64 + r, n - 1);
-      const size_t src = ((size_t)key * n_kv_heads + g) * kHeadDim + 8 * (c ^ ((r & 7) << 1));
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(v + src),
-                                       (__attribute__((address_space(3))) void*)(v_lds + i * 1024),
-                                       16, 0, 0);
-    }
+    const __amdgpu_buffer_rsrc_t r = rsrc(v, kb);
+    for (int i = w; i < 32; i += kCbWaves)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(v_lds + i * 1024), 16, v_vo,
+          2 * i * rstride, 0, 0);
   }
 };
 
+// l: the row's weight sum, formed on the matrix core as ones . P^T (every element of a
+// lane's l holds the sum of its query row).
 struct RowState {
-  float m_run, l_part;
+  float m_run;
+  v4f l;
   v4f acc[16];
 };
 
@@ -133,7 +142,7 @@ __device__ __forceinline__ void block_step(int kb, int nkb, const Loader& ld, co
   float x[16];
   float bmax = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) x[e] = S[e >> 2][e & 3] * qk_scale_log2;
+  for (int e = 0; e < 16; ++e) x[e] = S[e >> 2][e & 3];
   if (key0 + 64 > n || (causal && key0 + 63 > first_tok)) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -143,18 +152,20 @@ __device__ __forceinline__ void block_step(int kb, int nkb, const Loader& ld, co
         if (!(key < n && (!causal || key <= my_tok))) x[4 * t + i] = -INFINITY;
       }
   }
+  // The scale c > 0 goes into the exponent's fma: max(c s) = c max(s), and a masked
+  // s = -inf gives exp2(-inf) = 0.
 #pragma unroll
   for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, x[e]);
-  bmax = col_max(bmax);
+  bmax = col_max(bmax) * qk_scale_log2;
   if (__any(bmax > st.m_run + kLazyRescale)) {
     const float m_new = fmaxf(st.m_run, bmax);
     const float alpha = m_new == st.m_run ? 1.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) st.acc[dt] *= alpha;
-    st.l_part *= alpha;
+    st.l *= alpha;
     st.m_run = m_new;
   }
-  const float mu = st.m_run == -INFINITY ? 0.f : st.m_run;
+  const float nmu = st.m_run == -INFINITY ? 0.f : -st.m_run;
   // B operands of the two 32-key halves: h holds tiles 2h and 2h + 1 (elements 8h..8h+7).
   // hi = bf16(p) and lo = bf16(p - hi), both rounded to nearest even by the hardware
   // conversion (two values per instruction).
@@ -164,10 +175,8 @@ __device__ __forceinline__ void block_step(int kb, int nkb, const Loader& ld, co
     uint32_t hw[4], lw[4];
 #pragma unroll
     for (int j2 = 0; j2 < 4; ++j2) {
-      const float p0 = __builtin_amdgcn_exp2f(x[8 * h + 2 * j2] - mu);
-      const float p1 = __builtin_amdgcn_exp2f(x[8 * h + 2 * j2 + 1] - mu);
-      st.l_part += p0;
-      st.l_part += p1;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(x[8 * h + 2 * j2], qk_scale_log2, nmu));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(x[8 * h + 2 * j2 + 1], qk_scale_log2, nmu));
       const bf2 hi = {(__bf16)p0, (__bf16)p1};
       hw[j2] = __builtin_bit_cast(uint32_t, hi);
       const bf2 lo = {(__bf16)(p0 - __uint_as_float(hw[j2] << 16)),
@@ -195,6 +204,14 @@ __device__ __forceinline__ void block_step(int kb, int nkb, const Loader& ld, co
   v8bf va[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) va[h] = vop(0, h);
+  {
+    const v8bf ones = __builtin_bit_cast(v8bf, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      st.l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(v8bf, ph[h]), st.l, 0, 0, 0);
+      st.l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(v8bf, pl[h]), st.l, 0, 0, 0);
+    }
+  }
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) {
     v8bf vn[2];
@@ -281,7 +298,10 @@ __global__ __launch_bounds__(kCbThreads, 1) void chunk_bf16_kernel(
   __shared__ __align__(16) int8_t s_k0[kKBytes];
   __shared__ __align__(16) int8_t s_k1[kKBytes];
 
-  const Loader ld{k, v, n, n_kv_heads, g, w, lane};
+  const uint32_t rstride = (uint32_t)n_kv_heads * (kHeadDim * 2);
+  const int vh = lane >> 5;
+  const Loader ld{k, v, n, n_kv_heads, g, w, rstride, (uint32_t)lane * rstride,
+                  vh * rstride + 16 * ((lane & 31) ^ (((2 * w + vh) & 7) << 1))};
   {
     ld.issue_v(kb0, sv0);
     ld.issue_k(kb0, s_k0);
@@ -304,7 +324,7 @@ __global__ __launch_bounds__(kCbThreads, 1) void chunk_bf16_kernel(
 
     RowState st;
     st.m_run = -INFINITY;
-    st.l_part = 0.f;
+    st.l = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) st.acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
     const Block b0{s_k0, sv0}, b1{s_k1, sv1};
@@ -315,7 +335,7 @@ __global__ __launch_bounds__(kCbThreads, 1) void chunk_bf16_kernel(
         block_step(kb + 1, nkb, ld, qop, my_tok, t0, causal != 0, n, qk_scale_log2, gq, nn, vbase,
                    st, b1, b0);
     }
-    const float l = col_sum(st.l_part);
+    const float l = st.l[0];
     if (SPLIT && nkb_tile > sp.part_blocks) {  // a tile at or above row0: partial state
       if (my_tok < n) {
         const size_t pi = ((size_t)(my_tok - sp.row0) * n_q_heads + h) * sp.n_parts + part;
@@ -374,6 +394,8 @@ int launch_chunk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
                       int n_q_heads, int n_kv_heads, float sm_scale, float* out, float* ws,
                       hipStream_t stream) {
   const int n_qb = (n + kCbTok - 1) / kCbTok;
+  // The kernels need a scale > 0 (it multiplies the block max); sm_scale = 0 runs as 1e-30,
+  // which gives the same uniform weights in fp32.
   ChunkSplit sp{nullptr, nullptr, nullptr, 0, 1, 0};
   const int n_parts = ws != nullptr ? chunk_bf16_split_parts(n, causal, n_kv_heads, &sp.part_blocks) : 1;
   if (n_parts > 1) {
@@ -385,7 +407,7 @@ int launch_chunk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
     sp.ws_l = sp.ws_m + np;
     hipLaunchKernelGGL(chunk_bf16_kernel<1>, dim3((unsigned)(n_qb * n_kv_heads), (unsigned)n_parts),
                        dim3(kCbThreads), 0, stream, q, k, v, n, causal, n_q_heads, n_kv_heads,
-                       sm_scale * kLog2e, out, n_qb, 0, sp);
+                       fmaxf(sm_scale * kLog2e, 1e-30f), out, n_qb, 0, sp);
     int rc = check_launch("attn_chunk_bf16");
     if (rc) return rc;
     // rows row0.. : n - row0 rows at the tail of an n-key sequence (row t sees t + 1 keys)
@@ -396,7 +418,7 @@ int launch_chunk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
   const long long n_wg = xcd_per_head > 0 ? 8LL * ((n_qb + xcd_per_head - 1) / xcd_per_head)
                                           : (long long)n_qb * n_kv_heads;
   hipLaunchKernelGGL(chunk_bf16_kernel<0>, dim3((unsigned)n_wg), dim3(kCbThreads), 0, stream, q, k,
-                     v, n, causal, n_q_heads, n_kv_heads, sm_scale * kLog2e, out, n_qb,
+                     v, n, causal, n_q_heads, n_kv_heads, fmaxf(sm_scale * kLog2e, 1e-30f), out, n_qb,
                      xcd_per_head, sp);
   return check_launch("attn_chunk_bf16");
 }
