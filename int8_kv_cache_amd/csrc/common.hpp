@@ -93,6 +93,33 @@ __device__ __forceinline__ float wave_sum(float v) {
   return col_sum(v);
 }
 
+// Whole-wave max of values whose bit patterns order like the values (non-negative
+// floats), as unsigned integers: no NaN canonicalisation between the steps, and each DPP
+// step is one fused max.
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));   // [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));   // [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true));  // half mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true));  // mirror
+  return col_max_u(v);
+}
+
+// amax / 127 rounded to nearest even, as the IEEE fp32 division gives it. Inside
+// [2^-90, 2^127): q = RN(amax RN(1/127)) is within an ulp of the quotient, the remainder
+// amax - 127 q is exact in one fma (a normal number or 0 there), and one more fma with
+// RN(1/127) rounds q + rem / 127 correctly (Markstein's correction step; checked against
+// the division for every significand of the binades 2^-119 .. 2^127). Outside it (tiny,
+// huge, inf, NaN) the division itself.
+__device__ __forceinline__ float div127(float amax) {
+  constexpr float kR = 1.0f / 127.0f;
+  if (amax >= 0x1p-90f && amax < 0x1p127f) {
+    const float q = amax * kR;
+    const float rem = fmaf(-q, 127.0f, amax);
+    return fmaf(rem, kR, q);
+  }
+  return amax / 127.0f;
+}
+
 // Row quantizer for one row of 256 values spread over a wave, 4 per lane (lane l holds
 // elements 4l..4l+3). Rule: amax = max|x|, scale = amax/127 (IEEE fp32 division),
 // code = clamp(rint(x/scale), -127, 127) with x/scale the correctly rounded quotient and
@@ -102,17 +129,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ("INT8 KV and INT8 MMAC attention on a gfx936 DCU", §2.1.)
 __device__ __forceinline__ uint32_t quantize4(float x0, float x1, float x2, float x3,
                                               float* scale_out) {
-  float a = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
-  const float amax = wave_max(a);
-  const float scale = amax / 127.0f;
+  const uint32_t m = 0x7fffffffu;
+  const uint32_t a = max(max(__float_as_uint(x0) & m, __float_as_uint(x1) & m),
+                         max(__float_as_uint(x2) & m, __float_as_uint(x3) & m));
+  const float amax = __uint_as_float(wave_max_u(a));
+  const float scale = div127(amax);
   *scale_out = scale;
   if (scale == 0.0f) return 0u;
   // |x / scale| <= 127 (1 + 2^-23), so the codes need no clamp, and rint(v) of such a v
   // is fl(v + 1.5 * 2^23) - 1.5 * 2^23, whose fp32 bits carry the code's two's complement
-  // in their low byte. y = x * rcp(scale) lies within 2^-22 |y| of the correctly rounded
-  // x / scale, so the two round to the same integer unless y is that close to a
-  // half-integer; only then (and with a denormal scale, whose reciprocal is not finite)
-  // does the lane divide.
+  // in their low byte. The product x * rcp(scale) (reciprocal within an ulp) lies within
+  // 1.5 * 2^-23 * 127 < 2^-15 of the correctly rounded x / scale, so the two round to the
+  // same integer unless the product is within 2^-15 of a half-integer; the lane divides
+  // when it is within 2^-14 (and with a denormal scale, whose reciprocal is not finite).
   constexpr float kM = 12582912.0f;  // 1.5 * 2^23
   const float x[4] = {x0, x1, x2, x3};
   float t[4];
@@ -120,10 +149,9 @@ __device__ __forceinline__ uint32_t quantize4(float x0, float x1, float x2, floa
   const float r = __builtin_amdgcn_rcpf(scale);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float y = x[i] * r;
-    t[i] = y + kM;
-    const float e = y - (t[i] - kM);  // exact: y minus its nearest integer
-    slow |= fabsf(e) >= fmaf(fabsf(y), -0x1p-20f, 0.5f);
+    t[i] = fmaf(x[i], r, kM);                        // rint(x r) + 1.5 * 2^23
+    const float e = fmaf(x[i], r, -(t[i] - kM));     // x r minus its nearest integer
+    slow |= fabsf(e) >= 0.5f - 0x1p-14f;
   }
   if (slow) {
 #pragma unroll

@@ -28,10 +28,6 @@ __device__ __forceinline__ void load_row4(const void* base, size_t row, int lane
 // a multiple of 8, so a lane's 4 dims are all rotated or all passed through and all in
 // one half. Every product and sum is rounded on its own (no contraction into fma), the
 // fp32 rule the results are defined by.
-__device__ __forceinline__ float rot_first(float a, float c, float b, float s) {
-#pragma clang fp contract(off)
-  return a * c - b * s;
-}
 __device__ __forceinline__ float rot_second(float b, float c, float a, float s) {
 #pragma clang fp contract(off)
   return b * c + a * s;
@@ -55,7 +51,9 @@ __device__ __forceinline__ RopeLane rope_lane(const float* __restrict__ cs, int 
     const float4 c = *reinterpret_cast<const float4*>(cs + i0);
     const float4 sn = *reinterpret_cast<const float4*>(cs + half + i0);
     r.cc[0] = c.x; r.cc[1] = c.y; r.cc[2] = c.z; r.cc[3] = c.w;
-    r.ss[0] = sn.x; r.ss[1] = sn.y; r.ss[2] = sn.z; r.ss[3] = sn.w;
+    // The first half turns by -sin: a c - b s = a c + b (-s), the same rounding.
+    const float sg = r.first ? -1.0f : 1.0f;
+    r.ss[0] = sg * sn.x; r.ss[1] = sg * sn.y; r.ss[2] = sg * sn.z; r.ss[3] = sg * sn.w;
   }
   return r;
 }
@@ -65,8 +63,7 @@ __device__ __forceinline__ void rope4(float* x, const RopeLane& r) {
   for (int j = 0; j < 4; ++j) y[j] = __shfl(x[j], r.partner);
   if (r.in) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      x[j] = r.first ? rot_first(x[j], r.cc[j], y[j], r.ss[j]) : rot_second(x[j], r.cc[j], y[j], r.ss[j]);
+    for (int j = 0; j < 4; ++j) x[j] = rot_second(x[j], r.cc[j], y[j], r.ss[j]);
   }
 }
 
@@ -191,17 +188,18 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
     for (int i = 0; i < TPW; ++i) {
       const int t = tok0 + TPW * w + i;
       if (t >= n_tokens) break;  // whole wave
+      // The group's 6 rows are consecutive: one base per token, the rows at fixed offsets.
+      const size_t row0 = (size_t)t * pr.n_q_heads + head * kGroup;
 #pragma unroll
       for (int hh = 0; hh < kGroup; ++hh) {
         float* xr = qx[PRODUCE ? i : 0][hh];
         if (pr.rotary_dim > 0) rope4(xr, rl[PRODUCE ? i : 0]);
-        const size_t row = (size_t)t * pr.n_q_heads + head * kGroup + hh;
-        if (pr.q_rot != nullptr) store_bf16x4(pr.q_rot + row * kHeadDim + lane * 4, xr);
+        if (pr.q_rot != nullptr) store_bf16x4(pr.q_rot + row0 * kHeadDim + lane * 4 + hh * kHeadDim, xr);
         if (pr.q_codes != nullptr) {
           float sc;
           const uint32_t c = quantize4(xr[0], xr[1], xr[2], xr[3], &sc);
-          *reinterpret_cast<uint32_t*>(pr.q_codes + row * kHeadDim + lane * 4) = c;
-          if (lane == 0) pr.q_scales[row] = sc;
+          *reinterpret_cast<uint32_t*>(pr.q_codes + row0 * kHeadDim + lane * 4 + hh * kHeadDim) = c;
+          if (lane == 0) pr.q_scales[row0 + hh] = sc;
         }
       }
     }

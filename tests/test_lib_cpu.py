@@ -399,12 +399,13 @@ def test_attn_decode_noalloc_limits_on_the_host():
 
 
 def test_reciprocal_code_tie_band():
-    # The kernels take each code as rint(x * r), r the hardware reciprocal of the scale
-    # (within one ulp of 1 / scale), unless y = x * r lies within 2^-20 |y| of a
-    # half-integer, where they use the IEEE quotient x / scale. Checked here in numpy for
-    # reciprocals one ulp below, at and one ulp above the correctly rounded one: every
-    # element whose code from y differs from rint(x / scale) lies inside that band, on
-    # rows built to sit on and next to rounding ties at scales across the normal range.
+    # The kernels take each code as rint(x r), r the hardware reciprocal of the scale
+    # (within one ulp of 1 / scale), rounding the exact product x r once (an fma onto
+    # 1.5 * 2^23), unless x r lies within 2^-14 of a half-integer, where they use the IEEE
+    # quotient x / scale. Checked here in numpy for reciprocals one ulp below, at and one
+    # ulp above the correctly rounded one: every element whose code from x r differs from
+    # rint(x / scale) lies inside that band, on rows built to sit on and next to rounding
+    # ties at scales across the normal range.
     import numpy as np
     rng = np.random.default_rng(23)
     n_rows = 3000
@@ -426,9 +427,70 @@ def test_reciprocal_code_tie_band():
     r0 = (np.float32(1.0) / scale).astype(np.float32)
     misrounded = 0
     for r in (np.nextafter(r0, np.float32(0)), r0, np.nextafter(r0, np.float32(np.inf))):
-        y = (rows * r.astype(np.float32)[:, None]).astype(np.float32)
-        band = np.abs(np.abs(y - np.rint(y)) - np.float32(0.5)) <= np.abs(y) * np.float32(2.0 ** -20)
-        wrong = np.rint(y) != q_div
+        y = rows.astype(np.float64) * r.astype(np.float64)[:, None]  # exact products
+        n = np.rint(y)                                                 # ties to even
+        ef = (y - n).astype(np.float32)                                # one rounding
+        band = np.abs(ef) >= np.float32(0.5 - 2.0 ** -14)
+        wrong = n != q_div
         assert not np.any(wrong & ~band)
         misrounded += int(wrong.sum())
     assert misrounded > 1000   # the rows do reach the ties a plain reciprocal gets wrong
+
+
+def _rn32_of_sum(s, err):
+    # fp32 round-to-nearest-even of s + err, s float64 and |err| below half an ulp of s
+    # (the error term of an error-free sum): s rounds alone unless it sits exactly on an
+    # fp32 midpoint, where the sign of err decides.
+    import numpy as np
+    a = s.astype(np.float32)
+    lo = np.nextafter(a, np.float32(-np.inf))
+    hi = np.nextafter(a, np.float32(np.inf))
+    mid_lo = (a.astype(np.float64) + lo.astype(np.float64)) / 2
+    mid_hi = (a.astype(np.float64) + hi.astype(np.float64)) / 2
+    out = a.copy()
+    down = (s == mid_lo) & (err < 0)
+    up = (s == mid_hi) & (err > 0)
+    out[down] = lo[down]
+    out[up] = hi[up]
+    return out
+
+
+def _div127_corrected(x):
+    # The kernels' scale for amax in [2^-90, 2^127): q = RN(x RN(1/127)), rem = fma(-q,
+    # 127, x), scale = fma(rem, RN(1/127), q), every operation rounded once to fp32
+    # (nearest, ties to even), emulated exactly in float64.
+    import numpy as np
+    r = np.float32(1.0) / np.float32(127.0)
+    q = (x * r).astype(np.float32)
+    rem_exact = x.astype(np.float64) - 127.0 * q.astype(np.float64)  # exact in float64
+    rem = rem_exact.astype(np.float32)
+    assert np.array_equal(rem.astype(np.float64), rem_exact)         # the fma is exact
+    p = rem.astype(np.float64) * np.float64(r)                        # exact (24 x 24 bits)
+    s = q.astype(np.float64) + p
+    bb = s - q.astype(np.float64)
+    err = (q.astype(np.float64) - (s - bb)) + (p - bb)                # two-sum error
+    return _rn32_of_sum(s, err)
+
+
+def test_scale_division_by_127_corrected_product():
+    # The per-row scale amax / 127 must be the IEEE fp32 quotient. The kernels form it as a
+    # product with RN(1/127) corrected by one fma on the exact remainder. The rounding of
+    # that correction depends on the significand alone inside the range (no subnormal
+    # intermediate, no overflow), so every significand of one binade is checked against
+    # numpy's IEEE division, plus random values over the whole range; the uncorrected
+    # product is wrong for a few percent of them, which the check must see.
+    import numpy as np
+    rng = np.random.default_rng(127)
+    for part in range(4):
+        bits = np.uint32(127 << 23) + np.arange(part << 21, (part + 1) << 21, dtype=np.uint32)
+        x = bits.view(np.float32)
+        ref = x / np.float32(127.0)
+        got = _div127_corrected(x)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+        plain = (x * (np.float32(1.0) / np.float32(127.0))).astype(np.float32)
+        assert np.count_nonzero(plain != ref) > 50000
+    e = rng.integers(-90, 127, 1 << 20)
+    x = np.ldexp(1.0 + rng.random(1 << 20), e).astype(np.float32)
+    x = x[np.isfinite(x) & (x < np.float32(2.0 ** 127))]
+    got = _div127_corrected(x)
+    assert np.array_equal(got.view(np.uint32), (x / np.float32(127.0)).view(np.uint32))
