@@ -77,7 +77,9 @@ __device__ __forceinline__ void rope4(float* x, const RopeLane& r) {
 // scattered to its own slot.
 // With PRODUCE (kv_produce) the K rows are rotated by their token's position first, and
 // the workgroup also rotates and quantizes the query rows of the KV head's group for its
-// 16 tokens (each wave: its tokens, all 6 heads), codes row-major into q_codes.
+// 16 tokens (each wave: its tokens, all 6 heads), codes row-major into q_codes. PRODUCE = 2
+// is the common case compiled on its own (rotation, query codes, no bf16 copies): without
+// the per-row tests of those options the six query rows are straight-line code.
 struct Produce {
   const void* q;
   const int32_t* positions;
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
   // with the row loads and the compiler does not wait for it before issuing them.
   int posn[PRODUCE ? TPW : 1];
   if (PRODUCE) {
-    const int32_t* ppos = pr.rotary_dim > 0 ? pr.positions : slots;
+    const int32_t* ppos = (PRODUCE == 2 || pr.rotary_dim > 0) ? pr.positions : slots;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) posn[PRODUCE ? i : 0] = ppos[min(tok0 + TPW * w + i, n_tokens - 1)];
   }
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
   }
   // The RoPE rows of the tokens, ahead of the query rows in the load order.
   RopeLane rl[PRODUCE ? TPW : 1];
-  if (PRODUCE && pr.rotary_dim > 0) {
+  if (PRODUCE == 2 || (PRODUCE && pr.rotary_dim > 0)) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int pos = min(max(posn[PRODUCE ? i : 0], 0), pr.max_pos - 1);  // clamped: memory-safe
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
   // Query rows of the group for this wave's tokens, loaded with the K/V rows (one round
   // trip); tokens past the batch re-read the last one and are not stored.
   float qx[PRODUCE ? TPW : 1][kGroup][4];
-  const bool want_q = PRODUCE && (pr.q_codes != nullptr || pr.q_rot != nullptr);
+  const bool want_q = PRODUCE == 2 || (PRODUCE && (pr.q_codes != nullptr || pr.q_rot != nullptr));
   if (want_q) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
@@ -164,11 +166,11 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
     const int t = tok0 + (lane & 15);
     sl_run = t < n_tokens ? slots[t] : -1;
   }
-  if (PRODUCE && pr.rotary_dim > 0) {
+  if (PRODUCE == 2 || (PRODUCE && pr.rotary_dim > 0)) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) rope4(kx[i], rl[PRODUCE ? i : 0]);
   }
-  if (PRODUCE && pr.k_rot != nullptr) {
+  if (PRODUCE == 1 && pr.k_rot != nullptr) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int t = tok0 + TPW * w + i;
@@ -193,9 +195,9 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
 #pragma unroll
       for (int hh = 0; hh < kGroup; ++hh) {
         float* xr = qx[PRODUCE ? i : 0][hh];
-        if (pr.rotary_dim > 0) rope4(xr, rl[PRODUCE ? i : 0]);
-        if (pr.q_rot != nullptr) store_bf16x4(pr.q_rot + row0 * kHeadDim + lane * 4 + hh * kHeadDim, xr);
-        if (pr.q_codes != nullptr) {
+        if (PRODUCE == 2 || pr.rotary_dim > 0) rope4(xr, rl[PRODUCE ? i : 0]);
+        if (PRODUCE == 1 && pr.q_rot != nullptr) store_bf16x4(pr.q_rot + row0 * kHeadDim + lane * 4 + hh * kHeadDim, xr);
+        if (PRODUCE == 2 || pr.q_codes != nullptr) {
           float sc;
           const uint32_t c = quantize4(xr[0], xr[1], xr[2], xr[3], &sc);
           *reinterpret_cast<uint32_t*>(pr.q_codes + row0 * kHeadDim + lane * 4 + hh * kHeadDim) = c;
@@ -310,8 +312,17 @@ int launch_kv_produce(const void* q, const void* k, const void* v, int in_bf16, 
   const long long n_slots = (long long)num_pages * kPage;
   const Produce pr{q, positions, cos_sin, rotary_dim, max_pos, n_q_heads, q_codes, q_scales,
                    q_rot, k_rot};
-  if (in_bf16)
+  // The common case (rotation, int8 query codes, no bf16 copies) has its own instance
+  // with those tests compiled away.
+  const bool common = rotary_dim > 0 && q_codes != nullptr && q_rot == nullptr && k_rot == nullptr;
+  if (in_bf16 && common)
+    hipLaunchKernelGGL((kv_quant_write_kernel<1, 2, kProduceTpw>), grid, block, 0, stream, k, v, n_tokens,
+                       n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots, pr);
+  else if (in_bf16)
     hipLaunchKernelGGL((kv_quant_write_kernel<1, 1, kProduceTpw>), grid, block, 0, stream, k, v, n_tokens,
+                       n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots, pr);
+  else if (common)
+    hipLaunchKernelGGL((kv_quant_write_kernel<0, 2, kProduceTpw>), grid, block, 0, stream, k, v, n_tokens,
                        n_kv_heads, slots, k_cache, v_cache, k_scale, v_scale, n_slots, pr);
   else
     hipLaunchKernelGGL((kv_quant_write_kernel<0, 1, kProduceTpw>), grid, block, 0, stream, k, v, n_tokens,
