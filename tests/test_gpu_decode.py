@@ -145,7 +145,7 @@ def test_workspace_too_small_is_rejected():
     assert torch.all(out == 7.0)
 
 
-@pytest.mark.parametrize("n_kv", [1, 3])
+@pytest.mark.parametrize("n_kv", [1, 3, 8])
 def test_decode_other_kv_head_counts(n_kv):
     need_gpu()
     ctx = [1, 700, 1537]

@@ -68,6 +68,20 @@ def test_int8p_verify_rows(nq):
     _check(st, st.run_int8p(partition_rows=64))
 
 
+@pytest.mark.parametrize("n_kv,nq", [(1, 1), (3, 4), (8, 2)])
+def test_int8p_other_kv_head_counts(n_kv, nq):
+    # grid, tiles and merge at other group counts (6 query heads per KV head); the law picks
+    # the partition from the head count
+    need_gpu()
+    ctx = [nq, 40, 600, 1500]
+    case = workloads.make_decode_case(310 + n_kv, ctx, pages="random", k_outliers=4, extra_pages=2,
+                                      q_rows_per_seq=nq, n_q_heads=6 * n_kv, n_kv_heads=n_kv)
+    rows = lib.attn_decode_partition_rows(len(ctx), max(ctx), n_kv)
+    say(f"attn_decode_int8p nq={nq} contexts {ctx} with {n_kv} KV heads (partition {rows})")
+    st = DecodeSetup(case)
+    _check(st, st.run_int8p())
+
+
 def test_int8p_batch_flattened_grid():
     # 20 sequences with 512-key partitions: the flattened grid of real work items; the
     # same batch at 64-key partitions keeps the grid (both to the oracle), and rows before

@@ -39,6 +39,19 @@ def test_verify_ragged_contexts(nq):
     _check(st, st.run_verify())
 
 
+@pytest.mark.parametrize("n_kv,nq", [(1, 4), (3, 2), (8, 3)])
+def test_verify_other_kv_head_counts(n_kv, nq):
+    # the (partition, KV head, sequence) grid, the query-row tiles of a group and the merge's
+    # head index at other group counts (6 query heads per KV head)
+    need_gpu()
+    ctx = [nq, 40, 600, 1500]
+    say(f"attn_verify nq={nq} contexts {ctx} with {n_kv} KV heads x 6 query heads")
+    case = workloads.make_decode_case(300 + n_kv, ctx, pages="random", k_outliers=4, extra_pages=2,
+                                      q_rows_per_seq=nq, n_q_heads=6 * n_kv, n_kv_heads=n_kv)
+    st = DecodeSetup(case)
+    _check(st, st.run_verify())
+
+
 @pytest.mark.parametrize("nq", [2, 4])
 def test_verify_batch_flattened_grid(nq):
     # 24 sequences: the flattened grid of real work items (batches of 16 and more)
