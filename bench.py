@@ -221,8 +221,8 @@ def main():
                          "(reference dispatch for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build measures the single-GPU path "
-              "(see DESIGN.md for how it would shard); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: it measures one GPU's share of the work "
+              "(the library has no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
