@@ -147,12 +147,14 @@ __device__ __forceinline__ uint32_t quantize4(float x0, float x1, float x2, floa
   float t[4];
   bool slow = !(scale >= 0x1p-126f);
   const float r = __builtin_amdgcn_rcpf(scale);
+  float e[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    t[i] = fmaf(x[i], r, kM);                        // rint(x r) + 1.5 * 2^23
-    const float e = fmaf(x[i], r, -(t[i] - kM));     // x r minus its nearest integer
-    slow |= fabsf(e) >= 0.5f - 0x1p-14f;
+    t[i] = fmaf(x[i], r, kM);                  // rint(x r) + 1.5 * 2^23
+    e[i] = fmaf(x[i], r, -(t[i] - kM));        // x r minus its nearest integer
   }
+  // One compare for the lane's four (a NaN e, from a NaN x, fails it like before).
+  slow |= fmaxf(fmaxf(fabsf(e[0]), fabsf(e[1])), fmaxf(fabsf(e[2]), fabsf(e[3]))) >= 0.5f - 0x1p-14f;
   if (slow) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) t[i] = x[i] / scale + kM;

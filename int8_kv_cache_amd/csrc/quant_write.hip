@@ -110,7 +110,8 @@ __global__ __launch_bounds__(64 * 16 / TPW) void kv_quant_write_kernel(
     int8_t* __restrict__ v_cache, float* __restrict__ k_scale, float* __restrict__ v_scale,
     long long n_slots, Produce pr) {
   const int grp = blockIdx.x, head = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar row arithmetic
   const int tok0 = grp * 16;
   __shared__ int s_run;
   __shared__ __align__(16) uint32_t s_v[kBlockBytes / 4];  // V block [dim][token]
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(256) void q_quant_kernel(const uint16_t* __restrict
                                                       int8_t* __restrict__ codes,
                                                       float* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   if (row >= n_rows) return;
   float x[4];
   load_row4<1>(q, (size_t)row, lane, x);
