@@ -70,6 +70,36 @@ def test_chunk_bf16_split_equals_one_pass(n, n_kv):
     assert np.array_equal(a[:64], b[:64])
 
 
+@pytest.mark.parametrize("n,parted", [(3000, True), (6000, False)])
+def test_chunk_bf16_long_ragged_chunk(n, parted):
+    # long chunks with a ragged last block of 64 keys: at 3,000 rows the plan cuts the keys
+    # into partitions; at 6,000 rows (752 workgroups for 256 CUs) it keeps the one pass.
+    # 48 rows across the chunk, the last ones included, against exact attention on the
+    # same bf16 rows, and the default route against the one pass on every row
+    need_gpu()
+    ws = lib.attn_chunk_bf16_workspace_bytes(n, True, 24, 4)
+    say(f"attn_chunk_bf16 n={n} causal: split workspace {ws} B, 48 rows vs exact")
+    assert (ws > 0) == parted
+    rng = np.random.default_rng(270 + n)
+    q = rng.standard_normal((n, 24, 256), dtype=np.float32)
+    k = rng.standard_normal((n, 4, 256), dtype=np.float32)
+    k[:, :, rng.choice(256, 4, replace=False)] *= np.float32(10.0)
+    v = rng.standard_normal((n, 4, 256), dtype=np.float32)
+    qb, kb, vb = (workloads.f32_to_bf16_bits(a) for a in (q, k, v))
+    a = lib.attn_chunk_bf16(_bf16(qb), _bf16(kb), _bf16(vb), causal=True).cpu().numpy()
+    b = lib.attn_chunk_bf16(_bf16(qb), _bf16(kb), _bf16(vb), causal=True, split=False).cpu().numpy()
+    qd, kd, vd = (quant.bf16_bits_to_f32(x).astype(np.float64) for x in (qb, kb, vb))
+    rows = np.unique(np.concatenate([rng.choice(n, 40, replace=False), np.arange(n - 8, n)]))
+    ref = attention.attention_exact(qd[rows], kd, vd, 1 / 16, rows)
+    vmax = float(np.max(np.abs(vd)))
+    err = max(float(np.max(np.abs(a[rows] - ref))), float(np.max(np.abs(b[rows] - ref))))
+    d = float(np.max(np.abs(a - b)))
+    say(f"  err {err:.3e} (bound {TOL * vmax:.3e}); max |split - one pass| {d:.3e} "
+        f"(bound {1e-5 * vmax:.3e})")
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(b))
+    assert err <= TOL * vmax and d <= 1e-5 * vmax
+
+
 @pytest.mark.parametrize("n_kv", [1, 3])
 def test_chunk_bf16_other_kv_head_counts(n_kv):
     need_gpu()
