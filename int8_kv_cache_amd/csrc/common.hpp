@@ -107,9 +107,10 @@ __device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
 // amax / 127 rounded to nearest even, as the IEEE fp32 division gives it. Inside
 // [2^-90, 2^127): q = RN(amax RN(1/127)) is within an ulp of the quotient, the remainder
 // amax - 127 q is exact in one fma (a normal number or 0 there), and one more fma with
-// RN(1/127) rounds q + rem / 127 correctly (Markstein's correction step; checked against
-// the division for every significand of the binades 2^-119 .. 2^127). Outside it (tiny,
-// huge, inf, NaN) the division itself.
+// RN(1/127) rounds q + rem / 127 correctly (Markstein's correction step). The rounding
+// pattern repeats per binade inside the range; checked against the division for every
+// significand of a binade and for values across the range. Outside it (tiny, huge, inf,
+// NaN) the division itself.
 __device__ __forceinline__ float div127(float amax) {
   constexpr float kR = 1.0f / 127.0f;
   if (amax >= 0x1p-90f && amax < 0x1p127f) {
@@ -153,7 +154,7 @@ __device__ __forceinline__ uint32_t quantize4(float x0, float x1, float x2, floa
     t[i] = fmaf(x[i], r, kM);                  // rint(x r) + 1.5 * 2^23
     e[i] = fmaf(x[i], r, -(t[i] - kM));        // x r minus its nearest integer
   }
-  // One compare for the lane's four (a NaN e, from a NaN x, fails it like before).
+  // One compare for the lane's four.
   slow |= fmaxf(fmaxf(fabsf(e[0]), fabsf(e[1])), fmaxf(fabsf(e[2]), fabsf(e[3]))) >= 0.5f - 0x1p-14f;
   if (slow) {
 #pragma unroll
