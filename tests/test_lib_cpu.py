@@ -205,6 +205,11 @@ def test_kv_produce_and_q8_validation():
     assert cws(2048, True, 24, 4) == (2048 - 1280) * 24 * 2 * 258 * 4
     assert cws(2048, False, 24, 4) == 0                 # non-causal: one pass
     assert cws(64, True, 24, 4) == 0                    # one key block
+    # 3,000 rows: 2,256 blocks per head -> 36 per CU, partitions of 43 blocks (2,752 keys),
+    # 2 partitions over the 47 blocks, rows 2,752.. merged; 6,000 rows: 188 tiles x 4 heads
+    # keep the CUs busy and the plan keeps the one pass
+    assert cws(3000, True, 24, 4) == (3000 - 43 * 64) * 24 * 2 * 258 * 4
+    assert cws(6000, True, 24, 4) == 0
     need = cws(2048, True, 24, 4)
     cb = [FAKE, FAKE, FAKE, 2048, 1, 24, 4, 256, 0.0625, FAKE, FAKE, need - 1, None]
     assert L.attn_chunk_bf16(*cb) == C["I8A_EWORKSPACE"]
